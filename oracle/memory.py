@@ -1,0 +1,62 @@
+"""Per-rank model-state memory for data parallelism and ZeRO stages 1-3.  TEST INFRASTRUCTURE.
+
+[P1] "ZeRO 优化器的三个阶段深度对比", section 二, gives an estimator: per parameter, 2 bytes of
+16-bit parameters, 2 bytes of 16-bit gradients and 12 bytes of Adam state (fp32 copy, m, v); plain
+data parallelism keeps all three whole on every rank, ZeRO-1 divides the optimizer state by Nd,
+ZeRO-2 also the gradients, ZeRO-3 also the parameters; results in units of 1024**3 bytes. The same
+split is stated in section 一 and in [P3] "ZeRO Optimization", stages list. This module restates
+that rule in its own form: a table of which component each stage shards.
+
+``stage_bytes_exact`` is the integer variant for a concrete plan: a sharded component costs
+S (the padded shard size) elements per rank instead of N/Nd.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from .partition import Plan
+
+GIB = 1024 ** 3
+
+# stage -> which of (optimizer state, gradients, parameters) is divided over the Nd ranks
+STAGES = {
+    "DP": (False, False, False),
+    "ZeRO-1": (True, False, False),
+    "ZeRO-2": (True, True, False),
+    "ZeRO-3": (True, True, True),
+}
+
+
+@dataclass(frozen=True)
+class MemoryEstimation:
+    optimizer_states: float  # GiB per rank
+    gradients: float
+    parameters: float
+    total: float
+
+
+def estimate_memory_per_gpu(num_params: float, dp_degree: int, bytes_per_param: int = 2,
+                            bytes_per_opt_state: int = 12) -> dict[str, MemoryEstimation]:
+    """Per-rank GiB of each model-state component for every stage (gradients use the 16-bit size)."""
+    per_param = (bytes_per_opt_state, bytes_per_param, bytes_per_param)  # opt, grad, param
+    out = {}
+    for stage, sharded in STAGES.items():
+        comp = [num_params * b / (dp_degree if s else 1) for b, s in zip(per_param, sharded)]
+        out[stage] = MemoryEstimation(comp[0] / GIB, comp[1] / GIB, comp[2] / GIB, sum(comp) / GIB)
+    return out
+
+
+def stage_bytes_exact(plan: Plan, stage: int, param_b: int = 2, grad_b: int = 2,
+                      opt_b: int = 12) -> tuple[int, int, int, int]:
+    """(optimizer, gradient, parameter, total) bytes on one rank, integers; stage 0 = DP, 1..3."""
+    names = ("DP", "ZeRO-1", "ZeRO-2", "ZeRO-3")
+    if not 0 <= stage <= 3:
+        raise ValueError("stage must be 0..3")
+    sharded = STAGES[names[stage]]
+    comp = [b * (plan.shard_elems if s else plan.n)
+            for b, s in zip((opt_b, grad_b, param_b), sharded)]
+    total = sum(comp)
+    if total >= 1 << 64:
+        raise OverflowError("byte count does not fit in 64 bits")
+    return comp[0], comp[1], comp[2], total

@@ -1,0 +1,19 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long CPU test, deselect with -m 'not slow'")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests fail loudly when no GPU is present rather than silently passing; they are
+    # deselected on CPU-only hosts with -m "not gpu".
+    pass

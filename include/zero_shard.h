@@ -1,0 +1,173 @@
+/*
+ * zero_shard.h - one data-parallel rank's sharded optimizer step (ZeRO stages 1/2) on MI355X.
+ *
+ * The operation: a flattened, padded parameter space is split evenly over Nd data-parallel ranks;
+ * each rank keeps only its shard of the Adam state (fp32 parameter copy, m, v: 12 bytes per
+ * parameter), reduces the gradient for its shard only, updates its own parameters, and hands the
+ * 16-bit result to an all-gather that rebuilds the full parameter buffer on every rank.
+ * Sources, cited by page title and section:
+ *   "ZeRO 优化器的三个阶段深度对比：显存节省与通信开销的量化分析" (wmrh.cn), sections 一 and 二;
+ *   "ZeRO 优化器：把显存“分”着用" (5688vip.com), ZeRO Stage 1 and ZeRO Stage 2;
+ *   "ZeRO Optimization（零冗余优化）" (ai-master.cc glossary), core-operations and stages lists.
+ * The pages print no update equations and say nothing about loss scaling, overflow or clipping;
+ * the exact arithmetic below is this library's reading and is spelled out per entry point.
+ *
+ * Conventions for every entry point:
+ *   - Plain C ABI: sizes are element counts (uint64_t); pointers named d_* or documented as device
+ *     pointers must be device memory of the current HIP device; everything else is host memory.
+ *   - Ownership: the caller allocates and frees every buffer. The library allocates no memory and
+ *     keeps no state except a thread-local error message and a per-device launch-size cache.
+ *   - Streams: device work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and
+ *     never synchronised; device outputs are valid once the stream reaches that point.
+ *   - Errors: arguments are checked before any device work; on a bad argument nothing is launched
+ *     and nothing is written. A failed launch returns ZERO_E_HIP. Details: zero_last_error().
+ *   - n == 0 is valid and enqueues nothing (except where stated).
+ *   - Results are deterministic: a given input and size always produces the same bits.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_MAX_REPLICAS 64   /* gradient replicas one call can sum */
+#define ZERO_SQ_PARTIALS 2048  /* fp64 partial sums written by the squared-norm passes */
+
+typedef enum {
+  ZERO_OK = 0,
+  ZERO_E_INVAL = 1,       /* a null, out-of-range, aliased or inconsistent argument */
+  ZERO_E_OVERFLOW = 2,    /* a size or byte count does not fit in 64 bits */
+  ZERO_E_UNSUPPORTED = 3, /* a valid but unimplemented combination (e.g. fp32 parameter output) */
+  ZERO_E_HIP = 4          /* the HIP runtime reported an error */
+} zero_status;
+
+typedef enum { ZERO_F32 = 0, ZERO_F16 = 1, ZERO_BF16 = 2 } zero_dtype;
+
+typedef enum {
+  ZERO_ADAMW = 0,   /* decoupled decay: p *= (1 - lr*wd) before the Adam step */
+  ZERO_ADAM_L2 = 1  /* L2 decay: g += wd*p before the moments */
+} zero_wd_mode;
+
+/* Partition of N flat elements over nd ranks. */
+typedef struct {
+  uint64_t n;           /* real element count N */
+  uint64_t padded_n;    /* P = shard_elems * nd */
+  uint64_t shard_elems; /* S: elements per rank, padding included */
+  uint64_t pad;         /* P - N, all at the tail of the flat space */
+  uint32_t nd;          /* data-parallel degree */
+  uint32_t align_elems; /* S is a multiple of this */
+} zero_plan;
+
+/* A gradient source: `count` equally typed device arrays, each at least n elements, summed in
+ * ascending index order. `ptrs` is a host array of device pointers. Replicas may alias each other. */
+typedef struct {
+  const void* const* ptrs;
+  uint32_t count;  /* 1 .. ZERO_MAX_REPLICAS */
+  int32_t dtype;   /* zero_dtype */
+} zero_grad_src;
+
+/* Adam hyper-parameters, fp64 on the host; `step` is t >= 1 counting this step. */
+typedef struct {
+  double lr, beta1, beta2, eps, weight_decay;
+  int32_t wd_mode; /* zero_wd_mode */
+  int32_t reserved;
+  int64_t step;
+} zero_adam_hparams;
+
+/* fp32 step constants the kernels use, each rounded once from fp64 (see zero_adam_derive). */
+typedef struct {
+  float b1, b2;  /* beta1, beta2 */
+  float c1, c2;  /* 1 - beta1, 1 - beta2 */
+  float ss;      /* lr / (1 - beta1^t) */
+  float bc;      /* sqrt(1 - beta2^t) */
+  float e;       /* eps */
+  float dec;     /* 1 - lr*wd */
+  float w;       /* wd */
+} zero_adam_scalars;
+
+/* Even contiguous partition (P1 section 二; P3 stages list: each rank holds 1/Nd of the state).
+ * S = align_elems * ceil(ceil(n/nd) / align_elems), P = S*nd, pad = P - n. Rank r owns the flat
+ * range [r*S, (r+1)*S); padding sits at the tail; n < nd is allowed (trailing ranks own padding).
+ * Host only. Errors: out == NULL, nd == 0 or align_elems == 0 -> ZERO_E_INVAL; P >= 2^64 ->
+ * ZERO_E_OVERFLOW. */
+zero_status zero_partition_plan(uint64_t n, uint32_t nd, uint32_t align_elems, zero_plan* out);
+
+/* The range of rank `rank`: *begin = rank*S; *valid = min(S, max(0, n - begin)) real elements,
+ * the rest of the shard is padding. Host only. Errors: NULL pointers, rank >= nd, or a plan whose
+ * fields are inconsistent -> ZERO_E_INVAL. */
+zero_status zero_shard_range(const zero_plan* p, uint32_t rank, uint64_t* begin, uint64_t* valid);
+
+/* Per-rank model-state bytes of one stage (P1 sections 一/二: 16-bit parameters and gradients and
+ * 12 bytes of Adam state per parameter; DP keeps all whole, ZeRO-1 shards the optimizer state,
+ * ZeRO-2 also the gradients, ZeRO-3 also the parameters). A sharded component costs S elements,
+ * a whole one N. out[0..3] = optimizer, gradient, parameter, total bytes. stage: 0 = DP, 1..3.
+ * Host only. Errors: NULL, stage > 3 -> ZERO_E_INVAL; a byte count >= 2^64 -> ZERO_E_OVERFLOW. */
+zero_status zero_stage_bytes(const zero_plan* p, uint32_t stage, uint32_t param_b, uint32_t grad_b,
+                             uint32_t opt_b, uint64_t out[4]);
+
+/* The fp32 constants of step hp->step, each formed in fp64 and rounded once:
+ * b1 = f32(beta1), b2 = f32(beta2), c1 = f32(1-beta1), c2 = f32(1-beta2),
+ * ss = f32(lr / (1 - pow(beta1, t))), bc = f32(sqrt(1 - pow(beta2, t))), e = f32(eps),
+ * dec = f32(1 - lr*wd), w = f32(wd). Host only. Errors: NULL, step < 1, beta outside [0, 1),
+ * non-finite or negative lr/eps/wd, unknown wd_mode -> ZERO_E_INVAL. */
+zero_status zero_adam_derive(const zero_adam_hparams* hp, zero_adam_scalars* out);
+
+/* Reduction half of the gradient reduce-scatter, done over local replicas (P1 section 二; P2 ZeRO
+ * Stage 2): acc[i] = rep_0[i] + rep_1[i] + ... in ascending order, fp32 accumulator, each 16-bit
+ * replica widened exactly. Optional outputs, any subset but at least one:
+ *   out_grad      device float[n]: acc.
+ *   d_nonfinite   device int32: set to 1 if any acc[i] is +-inf or NaN, otherwise left as is
+ *                 (so several calls OR into it; the caller zeroes it first).
+ *   d_sq_partials device double[ZERO_SQ_PARTIALS]: every entry overwritten; their sum is
+ *                 sum_i (double(acc[i]) * sq_scale)^2 (finish with zero_shard_sqnorm).
+ * n == 0 still zeroes d_sq_partials when given. Aliasing: out_grad must not overlap a replica.
+ * Errors: bad source, no output, aliasing -> ZERO_E_INVAL; n*4 >= 2^64 -> ZERO_E_OVERFLOW. */
+zero_status zero_reduce_shard(const zero_grad_src* src, uint64_t n, float* out_grad,
+                              int32_t* d_nonfinite, double* d_sq_partials, double sq_scale,
+                              void* stream);
+
+/* Squared L2 norm of a shard in fp64, for gradient clipping. With d_grad != NULL, first writes
+ * the ZERO_SQ_PARTIALS partial sums of sum_i (double(d_grad[i]) * sq_scale)^2 into d_partials;
+ * with d_grad == NULL, d_partials must already hold them (from zero_reduce_shard). Then writes
+ * their sum, in a fixed order, to *d_out (device double). Errors: d_partials or d_out NULL ->
+ * ZERO_E_INVAL. */
+zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, double* d_partials,
+                              double* d_out, void* stream);
+
+/* One Adam/AdamW step on the rank's shard (P1 section 二: each rank updates only its own
+ * parameter subset with its own optimizer state; P2 ZeRO Stage 1/2), fused with the gradient
+ * reduction and the 16-bit cast into the rank's slot of the gathered buffer:
+ *   acc = sum of src replicas (as zero_reduce_shard); g = acc * grad_scale
+ *   [L2]    g = g + w*p
+ *   m = b1*m + c1*g;  v = b2*v + c2*(g*g);  den = sqrt(v)/bc + e
+ *   [AdamW] p = p*dec
+ *   p = p - ss*(m/den)
+ * every operation fp32, rounded to nearest even, no fused multiply-add, correctly rounded / and
+ * sqrt, constants from zero_adam_derive(hp). master, m, v (device float[n]) are updated in place.
+ * out_param (device, nullable): element i receives round-to-nearest-even(p[i]) as out_dtype
+ * (ZERO_BF16 or ZERO_F16); pass the full gathered buffer plus r*S to write rank r's slot.
+ * d_skip (device int32, nullable): when it holds a non-zero value at kernel start, nothing is
+ * written (the overflow-skip path: the caller then does not advance t).
+ * Aliasing: master, m, v, out_param must not overlap each other or any replica.
+ * Any alignment is accepted; 16-byte-aligned arrays take the vector path.
+ * Errors: NULLs, bad source, bad hparams, aliasing -> ZERO_E_INVAL; out_dtype ZERO_F32 ->
+ * ZERO_E_UNSUPPORTED; n*4 >= 2^64 -> ZERO_E_OVERFLOW. */
+zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float grad_scale,
+                                 float* master, float* m, float* v, const zero_adam_hparams* hp,
+                                 void* out_param, int32_t out_dtype, const int32_t* d_skip,
+                                 void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* zero_status_str(zero_status s);
+
+/* The detail of the last failing call on this thread ("" if none). */
+const char* zero_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

@@ -1,0 +1,169 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares, binds to torch's HIP
+runtime, and its host-only entry points match the oracle exactly. Device entry points are only
+called with arguments that fail validation (they return before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import zero_partition_plan_amd as Z
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "zero_shard.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:zero_status|const char\*)\s+(zero_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 9
+    L = Z.lib()
+    for name in names:
+        assert hasattr(L, name), name
+    # and the binding exposes the same names
+    for name in names:
+        assert callable(getattr(Z, name)), name
+
+
+def test_one_hip_runtime_in_process():
+    Z.lib()
+    maps = open("/proc/self/maps").read()
+    hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(hip) == 1, hip
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define ZERO_MAX_REPLICAS (\d+)", text).group(1)) == Z.ZERO_MAX_REPLICAS
+    assert int(re.search(r"#define ZERO_SQ_PARTIALS (\d+)", text).group(1)) == Z.ZERO_SQ_PARTIALS
+    assert ctypes.sizeof(Z.ZeroPlan) == 40 and ctypes.sizeof(Z.ZeroAdamHParams) == 56
+
+
+@pytest.mark.parametrize("align", (1, 2, 8, 64, 256))
+def test_plan_matches_oracle(align):
+    for n in list(range(0, 70)) + [299, 1_000_003, 6_738_415_616, 174_604_259_328, (1 << 63) + 5]:
+        for nd in (1, 2, 3, 4, 7, 8, 16, 17, 64):
+            try:
+                want = O.partition_plan(n, nd, align)
+            except OverflowError:
+                with pytest.raises(Z.ZeroError) as e:
+                    Z.zero_partition_plan(n, nd, align)
+                assert e.value.status == 2
+                continue
+            got = Z.zero_partition_plan(n, nd, align)
+            assert (got.n, got.padded_n, got.shard_elems, got.pad, got.nd, got.align_elems) == \
+                (want.n, want.padded_n, want.shard_elems, want.pad, want.nd, want.align_elems)
+            for r in sorted({0, nd // 2, nd - 1}):
+                assert Z.zero_shard_range(got, r) == O.shard_range(want, r)
+
+
+def test_plan_errors():
+    for args in ((10, 0, 1), (10, 2, 0)):
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_partition_plan(*args)
+        assert e.value.status == 1
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_partition_plan((1 << 64) - 1, 3, 1 << 31)
+    assert e.value.status == 2
+    p = Z.zero_partition_plan(100, 4)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_shard_range(p, 4)
+    bad = Z.ZeroPlan(100, 101, 25, 1, 4, 1)            # inconsistent: 25 * 4 != 101
+    with pytest.raises(Z.ZeroError):
+        Z.zero_shard_range(bad, 0)
+    assert "rank" in Z.zero_last_error() or "inconsistent" in Z.zero_last_error()
+
+
+def test_stage_bytes_match_oracle():
+    for n, nd in ((1_000_003, 4), (124_356_864, 8), (6_738_415_616, 8), (13_015_864_320, 16)):
+        p, op = Z.zero_partition_plan(n, nd), O.partition_plan(n, nd)
+        for stage in range(4):
+            for pb, gb, ob in ((2, 2, 12), (2, 4, 12), (4, 4, 8)):
+                assert Z.zero_stage_bytes(p, stage, pb, gb, ob) == O.stage_bytes_exact(op, stage, pb, gb, ob)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_stage_bytes(Z.zero_partition_plan(10, 2), 4)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_stage_bytes(Z.zero_partition_plan((1 << 62), 1), 0, 2, 2, 12)
+    assert e.value.status == 2
+
+
+def test_adam_scalars_match_oracle_bitwise():
+    rng = np.random.default_rng(9)
+    cases = [dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=t) for t in (1, 2, 11, 1000)]
+    for _ in range(200):
+        cases.append(dict(lr=float(10 ** rng.uniform(-6, -1)), beta1=float(rng.uniform(0, 0.99)),
+                          beta2=float(rng.uniform(0.9, 0.99999)), eps=float(10 ** rng.uniform(-12, -4)),
+                          weight_decay=float(rng.uniform(0, 0.3)), step=int(rng.integers(1, 100000))))
+    for c in cases:
+        got = Z.zero_adam_derive(Z.adam_hparams(**c))
+        want = O.adam_scalars(O.AdamHParams(**c))
+        for k in ("b1", "b2", "c1", "c2", "ss", "bc", "e", "dec", "w"):
+            assert np.float32(getattr(got, k)).view(np.uint32) == getattr(want, k).view(np.uint32), (k, c)
+
+
+def test_adam_derive_rejects_bad_hparams():
+    for bad in (dict(step=0), dict(beta1=1.0), dict(beta2=-0.1), dict(eps=-1.0),
+                dict(lr=float("nan")), dict(weight_decay=float("inf")), dict(wd_mode=7)):
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_adam_derive(Z.adam_hparams(**bad))
+        assert e.value.status == 1
+
+
+# Device entry points, called only with arguments that fail validation before any HIP call.
+
+def _src(ptrs, dtype=Z.ZERO_BF16):
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    return Z._GradSrc(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), len(ptrs), dtype), arr
+
+
+def test_device_entry_points_validate_first():
+    L = Z.lib()
+    hp = Z.adam_hparams()
+    fake = 1 << 40                                   # never dereferenced: every call below is invalid
+    ok_src, k1 = _src([fake])
+    # no replicas / too many / NULL replica / unknown dtype
+    for src, keep in (_src([]), _src([fake] * 65), _src([fake, 0]), _src([fake], 9)):
+        assert L.zero_adam_shard_step(ctypes.byref(src), 100, 1.0, fake + 4096, fake + 8192, fake + 12288,
+                                      ctypes.byref(hp), None, 0, None, None) == 1
+        assert L.zero_reduce_shard(ctypes.byref(src), 100, fake + 4096, None, None, 1.0, None) == 1
+    # NULL state
+    assert L.zero_adam_shard_step(ctypes.byref(ok_src), 100, 1.0, None, fake + 8192, fake + 12288,
+                                  ctypes.byref(hp), None, 0, None, None) == 1
+    # bad hparams
+    bad_hp = Z.adam_hparams(step=0)
+    assert L.zero_adam_shard_step(ctypes.byref(ok_src), 100, 1.0, fake + 4096, fake + 8192, fake + 12288,
+                                  ctypes.byref(bad_hp), None, 0, None, None) == 1
+    # fp32 output is unsupported; unknown output dtype is invalid
+    assert L.zero_adam_shard_step(ctypes.byref(ok_src), 100, 1.0, fake + 4096, fake + 8192, fake + 12288,
+                                  ctypes.byref(hp), fake + 16384, Z.ZERO_F32, None, None) == 3
+    assert L.zero_adam_shard_step(ctypes.byref(ok_src), 100, 1.0, fake + 4096, fake + 8192, fake + 12288,
+                                  ctypes.byref(hp), fake + 16384, 5, None, None) == 1
+    # aliasing: m overlaps master; out overlaps v; master overlaps a replica
+    assert L.zero_adam_shard_step(ctypes.byref(ok_src), 100, 1.0, fake + 4096, fake + 4096 + 396, fake + 12288,
+                                  ctypes.byref(hp), None, 0, None, None) == 1
+    assert L.zero_adam_shard_step(ctypes.byref(ok_src), 100, 1.0, fake + 4096, fake + 8192, fake + 12288,
+                                  ctypes.byref(hp), fake + 12288 + 100, Z.ZERO_BF16, None, None) == 1
+    assert L.zero_adam_shard_step(ctypes.byref(ok_src), 100, 1.0, fake + 100, fake + 8192, fake + 12288,
+                                  ctypes.byref(hp), None, 0, None, None) == 1
+    # size overflow
+    assert L.zero_adam_shard_step(ctypes.byref(ok_src), 1 << 62, 1.0, fake + 4096, fake + 8192, fake + 12288,
+                                  ctypes.byref(hp), None, 0, None, None) == 2
+    # reduce: no output requested; out_grad overlapping a replica
+    assert L.zero_reduce_shard(ctypes.byref(ok_src), 100, None, None, None, 1.0, None) == 1
+    assert L.zero_reduce_shard(ctypes.byref(ok_src), 100, fake + 8, None, None, 1.0, None) == 1
+    # sqnorm: NULL partials or out; out inside partials
+    assert L.zero_shard_sqnorm(None, 0, 1.0, None, fake, None) == 1
+    assert L.zero_shard_sqnorm(None, 0, 1.0, fake, fake + 8, None) == 1
+    assert "overlap" in Z.zero_last_error()
+
+
+def test_status_strings():
+    for s in range(5):
+        assert Z.zero_status_str(s)
+    assert Z.zero_status_str(99) == "unknown status"

@@ -1,0 +1,341 @@
+"""GPU parity of the fused sharded step and the reduce / squared-norm passes, at sizes the oracle
+finishes in seconds. Every comparison of fp32 state and 16-bit output is bit for bit (the library
+and the oracle evaluate the same fp32 operation order with IEEE rounding); the squared norm, an
+fp64 sum in a different order, is held to 1e-10 relative."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import zero_partition_plan_amd as Z
+from gpu_util import (DEV, assert_bits_equal, banner, bits16, bits32, dev_f32, dev_rep, empty16,
+                      f32_bits)
+from workloads import WORKLOADS
+from workloads import host as H
+
+pytestmark = pytest.mark.gpu
+
+TILE = 2048  # elements per block tile of the kernels (256 threads x 4 x 2)
+
+
+def _reps_np(rng, R, n, dtype, std=1e-3, valid=None):
+    x = (rng.standard_normal((R, n)).astype(np.float32) * np.float32(std))
+    if valid is not None:
+        x[:, valid:] = 0
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+    return (x * np.float32(64.0)).astype(np.float16).view(np.uint16)
+
+
+def _run_step(reps_np, dtype, n, master, m, v, hp_kw, out_dtype, grad_scale=1.0, offsets=(0, 0, 0, 0, 0)):
+    """Run the kernel on device copies placed at element offsets (rep, master, m, v, out) to reach
+    the aligned and misaligned paths; return (master, m, v, out16 or None) as numpy bit arrays."""
+    orep, op, om, ov, oo = offsets
+    R = reps_np.shape[0]
+    d_reps = [dev_rep(np.concatenate([np.zeros(orep, reps_np.dtype), r]), dtype)[orep:] for r in reps_np]
+    d_p = dev_f32(np.concatenate([np.zeros(op, np.float32), master]))[op:]
+    d_m = dev_f32(np.concatenate([np.zeros(om, np.float32), m]))[om:]
+    d_v = dev_f32(np.concatenate([np.zeros(ov, np.float32), v]))[ov:]
+    d_o = None
+    if out_dtype is not None:
+        d_o = empty16(n + oo + 5, out_dtype, fill=-3.0)
+    Z.zero_adam_shard_step(d_reps, n, grad_scale, d_p, d_m, d_v, Z.adam_hparams(**hp_kw),
+                           out=None if d_o is None else d_o[oo:oo + n])
+    torch.cuda.synchronize()
+    out = None
+    if d_o is not None:
+        full = bits16(d_o)
+        canary = O.cast_bf16_rne(np.float32([-3.0]))[0] if out_dtype == "bf16" else O.cast_fp16_rne(np.float32([-3.0]))[0]
+        assert (full[:oo] == canary).all() and (full[oo + n:] == canary).all(), "write outside the slot"
+        out = full[oo:oo + n]
+    return bits32(d_p), bits32(d_m), bits32(d_v), out
+
+
+def _check_step(reps_np, dtype, n, hp_kw, out_dtype, rng, grad_scale=1.0, offsets=(0, 0, 0, 0, 0),
+                warm=True):
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32) if warm else np.zeros(n, np.float32)
+    v = (rng.random(n) * 1e-7).astype(np.float32) if warm else np.zeros(n, np.float32)
+    got = _run_step(reps_np, dtype, n, master, m, v, hp_kw, out_dtype, grad_scale, offsets)
+    p2, m2, v2, o2 = O.sharded_step(list(reps_np), dtype, grad_scale, master, m, v,
+                                    O.AdamHParams(**hp_kw), out_dtype)
+    assert_bits_equal(got[0], f32_bits(p2), "master")
+    assert_bits_equal(got[1], f32_bits(m2), "m")
+    assert_bits_equal(got[2], f32_bits(v2), "v")
+    if out_dtype is not None:
+        assert_bits_equal(got[3], o2, "out")
+
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=3)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("R", [1, 2, 3, 8, 9, 16, 17, 64])
+def test_step_replica_counts_and_dtypes(dtype, R):
+    n = 3 * TILE + 1234                      # several full tiles and a ragged tail
+    banner(f"step dtype={dtype} R={R} n={n}")
+    rng = np.random.default_rng(100 + R)
+    _check_step(_reps_np(rng, R, n, dtype), dtype, n, HP, "bf16", rng)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16", None])
+@pytest.mark.parametrize("mode", ["adamw", "l2"])
+def test_step_outputs_and_decay_modes(out_dtype, mode):
+    n = 5 * TILE + 77
+    banner(f"step out={out_dtype} mode={mode}")
+    rng = np.random.default_rng(7)
+    hp = {**HP, "wd_mode": mode, "weight_decay": 0.05, "step": 1}
+    _check_step(_reps_np(rng, 8, n, "bf16"), "bf16", n, hp, out_dtype, rng, grad_scale=0.125)
+
+
+@pytest.mark.parametrize("offsets", [(1, 0, 0, 0, 0), (0, 1, 0, 0, 0), (0, 0, 2, 0, 0),
+                                     (0, 0, 0, 3, 0), (0, 0, 0, 0, 1), (3, 1, 2, 3, 5)])
+def test_step_misaligned_arrays(offsets):
+    n = 2 * TILE + 999
+    banner(f"step misaligned offsets={offsets}")
+    rng = np.random.default_rng(sum(offsets))
+    _check_step(_reps_np(rng, 3, n, "bf16"), "bf16", n, HP, "bf16", rng, offsets=offsets)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 1023, TILE - 1, TILE, TILE + 1])
+def test_step_small_and_edge_sizes(n):
+    banner(f"step n={n}")
+    rng = np.random.default_rng(n)
+    _check_step(_reps_np(rng, 4, n, "f16"), "f16", n, HP, "f16", rng)
+
+
+def test_step_n_zero_is_a_no_op():
+    d_p = dev_f32(np.ones(16, np.float32))
+    d_m = torch.zeros(16, device=DEV)
+    d_v = torch.zeros(16, device=DEV)
+    rep = dev_rep(np.ones(16, np.float32), "f32")
+    Z.zero_adam_shard_step([rep], 0, 1.0, d_p, d_m, d_v, Z.adam_hparams())
+    torch.cuda.synchronize()
+    assert (d_p.cpu().numpy() == 1).all() and not d_m.any() and not d_v.any()
+
+
+def test_tiny_workload_all_ranks_three_steps():
+    """The tiny workload: N = 1,000,003 over 4 ranks (one padding element), one fp32 gradient,
+    Adam 3 steps; every rank works on slices of shared flat buffers, so ranks 1-3 see element
+    offsets that are not 16-byte aligned. Results are gathered into one 16-bit buffer and compared
+    with the oracle's unsharded update, bit for bit, for both output formats."""
+    w = WORKLOADS["tiny"]
+    plan = Z.zero_partition_plan(w.n, w.nd)
+    S, P = plan.shard_elems, plan.padded_n
+    flat = H.flat_inputs(w, P)
+    for out_dtype in w.out_dtypes:
+        banner(f"tiny workload out={out_dtype}")
+        d_p = dev_f32(flat["master"])
+        d_m = torch.zeros(P, device=DEV)
+        d_v = torch.zeros(P, device=DEV)
+        d_g = dev_f32(flat["grad"])
+        d_out = empty16(P, out_dtype, fill=0.0)
+        p, m, v = flat["master"], np.zeros(P, np.float32), np.zeros(P, np.float32)
+        for t in range(1, w.steps + 1):
+            hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=t)
+            for r in range(w.nd):
+                b, _ = Z.zero_shard_range(plan, r)
+                Z.zero_adam_shard_step([d_g[b:b + S]], S, 1.0, d_p[b:b + S], d_m[b:b + S], d_v[b:b + S],
+                                       Z.adam_hparams(**hp), out=d_out[b:b + S])
+            torch.cuda.synchronize()
+            p, m, v, o = O.unsharded_step(flat["grad"], p, m, v, O.AdamHParams(**hp), out_dtype=out_dtype)
+            assert_bits_equal(bits32(d_p), f32_bits(p), f"master step {t}")
+            assert_bits_equal(bits32(d_m), f32_bits(m), f"m step {t}")
+            assert_bits_equal(bits32(d_v), f32_bits(v), f"v step {t}")
+            assert_bits_equal(bits16(d_out), o, f"gathered params step {t}")
+        assert bits32(d_p)[w.n:].tolist() == [0] * plan.pad      # padding stays 0
+
+
+def test_cast_edges_through_the_kernel():
+    """Zero gradient on zero state with wd = 0 leaves p unchanged, so the slot receives the cast of
+    arbitrary fp32 patterns: ties, subnormals, overflow, infinities, signed zeros."""
+    rng = np.random.default_rng(21)
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    pats = (hi[:, None] | lows[None, :]).reshape(-1)
+    pats = np.concatenate([pats, rng.integers(0, 1 << 32, 300_000, dtype=np.uint64).astype(np.uint32)])
+    x = pats.view(np.float32)
+    x = x[~np.isnan(x)].copy()
+    n = x.size
+    zero = np.zeros(n, np.float32)
+    for out_dtype, cast in (("bf16", O.cast_bf16_rne), ("f16", O.cast_fp16_rne)):
+        banner(f"cast edges {out_dtype} n={n}")
+        got = _run_step(np.zeros((1, n), np.float32), "f32", n, x, zero, zero,
+                        dict(lr=1e-3, weight_decay=0.0, step=1), out_dtype)
+        assert_bits_equal(got[0], f32_bits(x), "master unchanged")
+        assert_bits_equal(got[3], cast(x), f"cast {out_dtype}")
+
+
+def test_skip_flag():
+    n = 3 * TILE + 5
+    rng = np.random.default_rng(3)
+    reps = _reps_np(rng, 2, n, "bf16")
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    d_p, d_m, d_v = dev_f32(master), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    d_o = empty16(n, "bf16", fill=5.0)
+    d_r = [dev_rep(r, "bf16") for r in reps]
+    skip = torch.ones(1, dtype=torch.int32, device=DEV)
+    Z.zero_adam_shard_step(d_r, n, 1.0, d_p, d_m, d_v, Z.adam_hparams(), out=d_o, skip=skip)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits32(d_p), f32_bits(master), "skipped master")
+    assert not d_m.any() and not d_v.any() and (d_o == 5.0).all()
+    skip.zero_()
+    Z.zero_adam_shard_step(d_r, n, 1.0, d_p, d_m, d_v, Z.adam_hparams(), out=d_o, skip=skip)
+    torch.cuda.synchronize()
+    p2, _, _, o2 = O.sharded_step(list(reps), "bf16", 1.0, master, np.zeros(n, np.float32),
+                                  np.zeros(n, np.float32), O.AdamHParams(), "bf16")
+    assert_bits_equal(bits32(d_p), f32_bits(p2), "stepped master")
+    assert_bits_equal(bits16(d_o), o2, "stepped out")
+
+
+def test_repeat_runs_are_bitwise_identical():
+    n = 7 * TILE + 11
+    rng = np.random.default_rng(4)
+    reps = _reps_np(rng, 8, n, "bf16")
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    z = np.zeros(n, np.float32)
+    a = _run_step(reps, "bf16", n, master, z, z, HP, "bf16")
+    b = _run_step(reps, "bf16", n, master, z, z, HP, "bf16")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+# ------------------------------------------------------------------ reduce and squared norm
+
+def _reduce(reps_np, dtype, n, sq_scale=1.0, want_grad=True, offset=0):
+    d_r = [dev_rep(np.concatenate([np.zeros(offset, reps_np.dtype), r]), dtype)[offset:] for r in reps_np]
+    d_g = torch.full((n + offset,), 7.0, device=DEV)[offset:] if want_grad else None
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    parts = torch.full((Z.ZERO_SQ_PARTIALS,), 9.0, dtype=torch.float64, device=DEV)
+    out = torch.zeros(1, dtype=torch.float64, device=DEV)
+    Z.zero_reduce_shard(d_r, n, d_g, flag, parts, sq_scale)
+    Z.zero_shard_sqnorm(None, n, sq_scale, parts, out)
+    torch.cuda.synchronize()
+    return (None if d_g is None else bits32(d_g)), int(flag.item()), float(out.item()), parts.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("R", [1, 3, 8, 16, 64])
+def test_reduce_matches_oracle(dtype, R):
+    n = 9 * TILE + 333
+    banner(f"reduce dtype={dtype} R={R}")
+    rng = np.random.default_rng(200 + R)
+    reps = _reps_np(rng, R, n, dtype)
+    g, flag, sq, _ = _reduce(reps, dtype, n, sq_scale=2.0 ** -6)
+    acc = O.replica_sum(list(reps), dtype)
+    assert_bits_equal(g, f32_bits(acc), "reduced grad")
+    assert flag == 0
+    assert sq == pytest.approx(O.shard_sqnorm(acc, 2.0 ** -6), rel=1e-10, abs=0)
+
+
+@pytest.mark.parametrize("n", [1, 5, TILE - 1, TILE + 3, 5000 * TILE + 17])
+def test_reduce_sizes_and_misalignment(n):
+    banner(f"reduce n={n}")
+    rng = np.random.default_rng(n % 1000)
+    reps = _reps_np(rng, 2, n, "bf16")
+    acc = O.replica_sum(list(reps), "bf16")
+    for offset in (0, 1):
+        g, flag, sq, _ = _reduce(reps, "bf16", n, offset=offset)
+        assert_bits_equal(g, f32_bits(acc), f"reduced grad offset {offset}")
+        assert sq == pytest.approx(O.shard_sqnorm(acc), rel=1e-10, abs=0)
+
+
+def test_reduce_zero_size_zeroes_partials():
+    reps = np.zeros((1, 4), np.float32)
+    _, flag, sq, parts = _reduce(reps, "f32", 0)
+    assert sq == 0.0 and flag == 0 and not parts.any()
+
+
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
+def test_reduce_flags_nonfinite(bad):
+    n = 4 * TILE + 9
+    rng = np.random.default_rng(5)
+    reps = _reps_np(rng, 3, n, "f32")
+    for pos in (0, 2 * TILE + 17, n - 1):           # vector tile and ragged tail
+        r = reps.copy()
+        r[1, pos] = bad
+        _, flag, _, _ = _reduce(r, "f32", n, want_grad=False)
+        assert flag == 1
+    # +inf and -inf in two replicas sum to NaN: still flagged
+    r = reps.copy()
+    r[0, 5], r[2, 5] = np.inf, -np.inf
+    assert _reduce(r, "f32", n)[1] == 1
+
+
+def test_reduce_is_deterministic():
+    n = 3000 * TILE + 3
+    rng = np.random.default_rng(6)
+    reps = _reps_np(rng, 4, n, "f16")
+    a = _reduce(reps, "f16", n, sq_scale=2.0 ** -16)
+    b = _reduce(reps, "f16", n, sq_scale=2.0 ** -16)
+    assert np.array_equal(a[0], b[0]) and a[2] == b[2] and np.array_equal(a[3], b[3])
+
+
+def test_sqnorm_from_fp32_grad():
+    for n in (1, 1000, 77 * TILE + 5):
+        rng = np.random.default_rng(n)
+        g = (rng.standard_normal(n) * 3).astype(np.float32)
+        parts = torch.zeros(Z.ZERO_SQ_PARTIALS, dtype=torch.float64, device=DEV)
+        out = torch.zeros(1, dtype=torch.float64, device=DEV)
+        Z.zero_shard_sqnorm(dev_f32(g), n, 0.5, parts, out)
+        torch.cuda.synchronize()
+        assert float(out.item()) == pytest.approx(O.shard_sqnorm(g, 0.5), rel=1e-10, abs=0)
+
+
+# ------------------------------------------------------------------ two-pass clip / overflow path
+
+def _two_pass(reps_np, n, master, loss_scale, max_norm, hp_kw):
+    """reduce (grad, flag, partials) -> sqnorm -> host coef -> step with skip flag."""
+    d_r = [dev_rep(r, "f16") for r in reps_np]
+    d_g = torch.empty(n, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    parts = torch.empty(Z.ZERO_SQ_PARTIALS, dtype=torch.float64, device=DEV)
+    sq = torch.empty(1, dtype=torch.float64, device=DEV)
+    Z.zero_reduce_shard(d_r, n, d_g, flag, parts, 1.0 / loss_scale)
+    Z.zero_shard_sqnorm(None, n, 1.0 / loss_scale, parts, sq)
+    flag_h, sq_h = int(flag.item()), float(sq.item())
+    coef = O.clip_coefficient(sq_h, max_norm) if flag_h == 0 else 1.0
+    gs = float(np.float32(coef / loss_scale))
+    d_p, d_m, d_v = dev_f32(master), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    d_o = empty16(n, "f16", fill=0.0)
+    Z.zero_adam_shard_step([d_g], n, gs, d_p, d_m, d_v, Z.adam_hparams(**hp_kw), out=d_o, skip=flag)
+    torch.cuda.synchronize()
+    return flag_h, sq_h, gs, bits32(d_p), bits32(d_m), bits32(d_v), bits16(d_o)
+
+
+@pytest.mark.parametrize("inject", [False, True])
+def test_two_pass_clip_and_overflow_skip(inject):
+    """fp16 replicas holding grad * 2^16: unscale, squared norm, clip coefficient from the host,
+    AdamW; with an injected +inf the whole step is skipped and the state stays bit-identical."""
+    n, R, ls = 6 * TILE + 321, 16, 65536.0
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((R, n)).astype(np.float32) * np.float32(1e-4)
+    reps = (x * np.float32(ls)).astype(np.float16).view(np.uint16)
+    if inject:
+        reps[5, 1234] = 0x7C00
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    hp = dict(lr=1e-3, weight_decay=0.01, step=1)
+    flag, sq, gs, p, m, v, o = _two_pass(reps, n, master, ls, 0.01, hp)
+    acc = O.replica_sum(list(reps), "f16")
+    assert flag == int(O.nonfinite_flag(acc))
+    if inject:
+        assert_bits_equal(p, f32_bits(master), "skipped master")
+        assert not m.any() and not v.any() and not o.any()
+        return
+    want_sq = O.shard_sqnorm(acc, 1.0 / ls)
+    assert sq == pytest.approx(want_sq, rel=1e-10, abs=0)
+    coef = O.clip_coefficient(want_sq, 0.01)
+    assert coef < 1.0                                   # clipping is active in this case
+    # the scale the pipeline used agrees with the oracle's to within one fp32 ulp; the update is
+    # then checked bit for bit with that same scale
+    want_gs = np.float32(coef / ls)
+    assert abs(np.float32(gs) - want_gs) <= np.spacing(want_gs)
+    p2, m2, v2, o2 = O.sharded_step([acc], "f32", gs, master, np.zeros(n, np.float32),
+                                    np.zeros(n, np.float32), O.AdamHParams(**hp), "f16")
+    assert_bits_equal(p, f32_bits(p2), "master")
+    assert_bits_equal(m, f32_bits(m2), "m")
+    assert_bits_equal(v, f32_bits(v2), "v")
+    assert_bits_equal(o, o2, "fp16 params")

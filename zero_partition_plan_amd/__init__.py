@@ -1,0 +1,220 @@
+"""Python binding of libzero_shard: one data-parallel rank's sharded ZeRO optimizer step on MI355X.
+
+Argument marshalling only. Every step of the path runs in the HIP kernels of libzero_shard.so;
+torch supplies device memory and the stream. The entry points carry the names of the C ABI in
+``include/zero_shard.h``, where each one's arithmetic, layout, ownership and errors are stated.
+
+The library must be built (``python -m zero_partition_plan_amd.build``); importing this package
+without it raises, there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loaded first so the library binds to the HIP runtime torch uses)
+
+__all__ = [
+    "ZeroError", "ZeroPlan", "ZeroAdamHParams", "ZeroAdamScalars", "lib", "lib_path",
+    "ZERO_MAX_REPLICAS", "ZERO_SQ_PARTIALS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
+    "ZERO_ADAMW", "ZERO_ADAM_L2", "adam_hparams",
+    "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_adam_derive",
+    "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
+    "zero_status_str", "zero_last_error",
+]
+
+ZERO_MAX_REPLICAS = 64
+ZERO_SQ_PARTIALS = 2048
+ZERO_OK, ZERO_E_INVAL, ZERO_E_OVERFLOW, ZERO_E_UNSUPPORTED, ZERO_E_HIP = range(5)
+ZERO_F32, ZERO_F16, ZERO_BF16 = 0, 1, 2
+ZERO_ADAMW, ZERO_ADAM_L2 = 0, 1
+
+_TORCH_DT = {torch.float32: ZERO_F32, torch.float16: ZERO_F16, torch.bfloat16: ZERO_BF16}
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {zero_status_str(status)} ({detail})")
+
+
+class ZeroPlan(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint64), ("padded_n", ctypes.c_uint64),
+                ("shard_elems", ctypes.c_uint64), ("pad", ctypes.c_uint64),
+                ("nd", ctypes.c_uint32), ("align_elems", ctypes.c_uint32)]
+
+    def __repr__(self):
+        return (f"ZeroPlan(n={self.n}, padded_n={self.padded_n}, shard_elems={self.shard_elems}, "
+                f"pad={self.pad}, nd={self.nd}, align_elems={self.align_elems})")
+
+
+class _GradSrc(ctypes.Structure):
+    _fields_ = [("ptrs", ctypes.POINTER(ctypes.c_void_p)), ("count", ctypes.c_uint32),
+                ("dtype", ctypes.c_int32)]
+
+
+class ZeroAdamHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("wd_mode", ctypes.c_int32), ("reserved", ctypes.c_int32), ("step", ctypes.c_int64)]
+
+
+class ZeroAdamScalars(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_float) for k in ("b1", "b2", "c1", "c2", "ss", "bc", "e", "dec", "w")]
+
+
+def adam_hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, wd_mode="adamw",
+                 step=1) -> ZeroAdamHParams:
+    mode = {"adamw": ZERO_ADAMW, "l2": ZERO_ADAM_L2}.get(wd_mode, wd_mode)
+    return ZeroAdamHParams(lr, beta1, beta2, eps, weight_decay, int(mode), 0, int(step))
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.environ.get("ZERO_SHARD_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "libzero_shard.so")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run `python -m zero_partition_plan_amd.build`")
+        L = ctypes.CDLL(path)
+        u64, u32, i32, vp = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int32, ctypes.c_void_p
+        P = ctypes.POINTER
+        sig = {
+            "zero_partition_plan": [u64, u32, u32, P(ZeroPlan)],
+            "zero_shard_range": [P(ZeroPlan), u32, P(u64), P(u64)],
+            "zero_stage_bytes": [P(ZeroPlan), u32, u32, u32, u32, P(u64)],
+            "zero_adam_derive": [P(ZeroAdamHParams), P(ZeroAdamScalars)],
+            "zero_reduce_shard": [P(_GradSrc), u64, vp, vp, vp, ctypes.c_double, vp],
+            "zero_shard_sqnorm": [vp, u64, ctypes.c_double, vp, vp, vp],
+            "zero_adam_shard_step": [P(_GradSrc), u64, ctypes.c_float, vp, vp, vp,
+                                     P(ZeroAdamHParams), vp, i32, vp, vp],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.zero_status_str.argtypes = [ctypes.c_int]
+        L.zero_status_str.restype = ctypes.c_char_p
+        L.zero_last_error.argtypes = []
+        L.zero_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def zero_status_str(status: int) -> str:
+    return lib().zero_status_str(status).decode()
+
+
+def zero_last_error() -> str:
+    return lib().zero_last_error().decode()
+
+
+def _check(status: int, fn: str):
+    if status != ZERO_OK:
+        raise ZeroError(status, fn, zero_last_error())
+
+
+# ------------------------------------------------------------------------------ host-only calls
+
+def zero_partition_plan(n: int, nd: int, align_elems: int = 1) -> ZeroPlan:
+    p = ZeroPlan()
+    _check(lib().zero_partition_plan(n, nd, align_elems, ctypes.byref(p)), "zero_partition_plan")
+    return p
+
+
+def zero_shard_range(plan: ZeroPlan, rank: int) -> tuple[int, int]:
+    b, v = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib().zero_shard_range(ctypes.byref(plan), rank, ctypes.byref(b), ctypes.byref(v)),
+           "zero_shard_range")
+    return b.value, v.value
+
+
+def zero_stage_bytes(plan: ZeroPlan, stage: int, param_b: int = 2, grad_b: int = 2,
+                     opt_b: int = 12) -> tuple[int, int, int, int]:
+    out = (ctypes.c_uint64 * 4)()
+    _check(lib().zero_stage_bytes(ctypes.byref(plan), stage, param_b, grad_b, opt_b, out),
+           "zero_stage_bytes")
+    return tuple(int(x) for x in out)
+
+
+def zero_adam_derive(hp: ZeroAdamHParams) -> ZeroAdamScalars:
+    out = ZeroAdamScalars()
+    _check(lib().zero_adam_derive(ctypes.byref(hp), ctypes.byref(out)), "zero_adam_derive")
+    return out
+
+
+# ------------------------------------------------------------------------------ device calls
+
+def _ptr(t, n: int, what: str, dtype=None) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a device tensor")
+    if dtype is not None and t.dtype not in dtype:
+        raise TypeError(f"{what}: dtype {t.dtype} not in {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{what} holds {t.numel()} elements, {n} needed")
+    return t.data_ptr()
+
+
+def _src(reps, n: int):
+    """Replica list (or a 2-D tensor whose rows are replicas) -> C gradient source."""
+    rows = list(reps.unbind(0)) if isinstance(reps, torch.Tensor) and reps.dim() == 2 else list(reps)
+    if not rows:
+        raise ValueError("no gradient replicas")
+    dt = rows[0].dtype
+    if dt not in _TORCH_DT or any(r.dtype != dt for r in rows):
+        raise TypeError("replicas must share one of float32, float16, bfloat16")
+    arr = (ctypes.c_void_p * len(rows))(*[_ptr(r, n, f"replica {k}") for k, r in enumerate(rows)])
+    return _GradSrc(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), len(rows), _TORCH_DT[dt]), arr
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def zero_reduce_shard(reps, n: int, out_grad=None, nonfinite=None, sq_partials=None,
+                      sq_scale: float = 1.0, stream=None):
+    src, keep = _src(reps, n)
+    _check(lib().zero_reduce_shard(
+        ctypes.byref(src), n, _ptr(out_grad, n, "out_grad", (torch.float32,)),
+        _ptr(nonfinite, 1, "nonfinite", (torch.int32,)),
+        _ptr(sq_partials, ZERO_SQ_PARTIALS, "sq_partials", (torch.float64,)),
+        float(sq_scale), _stream(stream)), "zero_reduce_shard")
+
+
+def zero_shard_sqnorm(grad, n: int, sq_scale: float, partials, out, stream=None):
+    _check(lib().zero_shard_sqnorm(
+        _ptr(grad, n, "grad", (torch.float32,)), n, float(sq_scale),
+        _ptr(partials, ZERO_SQ_PARTIALS, "partials", (torch.float64,)),
+        _ptr(out, 1, "out", (torch.float64,)), _stream(stream)), "zero_shard_sqnorm")
+
+
+def zero_adam_shard_step(reps, n: int, grad_scale: float, master, m, v, hp: ZeroAdamHParams,
+                         out=None, skip=None, stream=None):
+    """``out``: bf16/fp16 device tensor view starting at the rank's slot (or None)."""
+    src, keep = _src(reps, n)
+    f32 = (torch.float32,)
+    out_dt = ZERO_F32
+    if out is not None:
+        if out.dtype not in (torch.bfloat16, torch.float16):
+            raise TypeError("out must be bfloat16 or float16")
+        out_dt = _TORCH_DT[out.dtype]
+    _check(lib().zero_adam_shard_step(
+        ctypes.byref(src), n, float(grad_scale), _ptr(master, n, "master", f32),
+        _ptr(m, n, "m", f32), _ptr(v, n, "v", f32), ctypes.byref(hp),
+        _ptr(out, n, "out"), out_dt, _ptr(skip, 1, "skip", (torch.int32,)), _stream(stream)),
+        "zero_adam_shard_step")

@@ -1,0 +1,602 @@
+// gfx950 kernels of the per-rank sharded optimizer step and their C-ABI launchers.
+//
+// Everything here is HBM-bound elementwise streaming (about 0.5 flop per byte), so nothing is
+// shaped for MFMA. Each block owns contiguous tiles of kTile elements; inside a tile a thread owns
+// kSub groups of 4 consecutive elements spaced kBlock*4 apart, so every load instruction of a
+// wave covers one contiguous 1 KiB (fp32) or 512 B (16-bit) run. Full tiles whose arrays are all
+// 16-byte aligned take that vector path; the ragged last tile and misaligned arrays take a
+// per-element path with the same arithmetic.
+//
+// Arithmetic is fp32 with every operation rounded on its own: the library is built with
+// -ffp-contract=off and HIP's correctly rounded fp32 division and square root, so the results
+// equal a plain IEEE evaluation of the same expression order bit for bit.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_internal.h"
+
+#ifndef ZERO_ADAM_SUB
+#define ZERO_ADAM_SUB 2            // 4-element groups per thread per tile in the Adam kernel
+#endif
+#ifndef ZERO_REDUCE_SUB
+#define ZERO_REDUCE_SUB 2          // same for the reduce / squared-norm kernel
+#endif
+#ifndef ZERO_ADAM_BLOCKS_PER_CU
+#define ZERO_ADAM_BLOCKS_PER_CU 0  // 0: one tile per block; k > 0: grid-stride over k*CUs blocks
+#endif
+#ifndef ZERO_NT
+#define ZERO_NT 1                  // streaming (non-temporal) loads and stores: data is touched once
+#endif
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct RepPtrs {
+  const void* p[ZERO_MAX_REPLICAS];
+};
+
+struct StepScalars {
+  float gs;  // grad_scale
+  float b1, b2, c1, c2, ss, bc, e, dec, w;
+};
+
+// ---------------------------------------------------------------------------------------------
+// memory helpers
+
+template <typename T>
+__device__ __forceinline__ T ld(const T* p) {
+#if ZERO_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ void st(T* p, T v) {
+#if ZERO_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// fp32 -> bf16, round to nearest even; NaN keeps sign and top payload and is made quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// fp32 -> IEEE binary16, round to nearest even (the hardware conversion in the default mode).
+__device__ __forceinline__ uint32_t f32_to_f16(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// 4 consecutive replica elements starting at element i (vector path: i is a multiple of 4 and
+// the array is aligned to 4 elements).
+template <int RDT>
+__device__ __forceinline__ f32x4 ld_rep4(const void* base, uint64_t i) {
+  if constexpr (RDT == ZERO_F32) {
+    return ld(reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i));
+  } else {
+    const u32x2 w = ld(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + i));
+    f32x4 r;
+    if constexpr (RDT == ZERO_BF16) {
+      r.x = __uint_as_float(w.x << 16);
+      r.y = __uint_as_float(w.x & 0xffff0000u);
+      r.z = __uint_as_float(w.y << 16);
+      r.w = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+      r.x = f16_to_f32(w.x & 0xffffu);
+      r.y = f16_to_f32(w.x >> 16);
+      r.z = f16_to_f32(w.y & 0xffffu);
+      r.w = f16_to_f32(w.y >> 16);
+    }
+    return r;
+  }
+}
+
+template <int RDT>
+__device__ __forceinline__ float ld_rep1(const void* base, uint64_t i) {
+  if constexpr (RDT == ZERO_F32) return static_cast<const float*>(base)[i];
+  else if constexpr (RDT == ZERO_BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
+  else return f16_to_f32(static_cast<const uint16_t*>(base)[i]);
+}
+
+template <int ODT>
+__device__ __forceinline__ uint32_t to_out(float x) {
+  if constexpr (ODT == ZERO_BF16) return f32_to_bf16(x);
+  else return f32_to_f16(x);
+}
+
+// ---------------------------------------------------------------------------------------------
+// replica sum: acc = rep_0 + rep_1 + ... in ascending order (loads issued 8 replicas at a time)
+
+template <int RDT, int RFIX, int SUB>
+__device__ __forceinline__ void sum_reps4(const RepPtrs& reps, int nrep, const uint64_t (&idx)[SUB],
+                                          f32x4 (&acc)[SUB]) {
+  const int R = RFIX ? RFIX : nrep;
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) acc[u] = ld_rep4<RDT>(reps.p[0], idx[u]);
+  for (int k0 = 1; k0 < R; k0 += 8) {
+    f32x4 t[8][SUB];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < R) {
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) t[j][u] = ld_rep4<RDT>(reps.p[k0 + j], idx[u]);
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < R) {
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) acc[u] = acc[u] + t[j][u];
+      }
+  }
+}
+
+template <int RDT>
+__device__ __forceinline__ float sum_reps1(const RepPtrs& reps, int nrep, uint64_t i) {
+  float a = ld_rep1<RDT>(reps.p[0], i);
+  for (int k = 1; k < nrep; ++k) a = a + ld_rep1<RDT>(reps.p[k], i);
+  return a;
+}
+
+// ---------------------------------------------------------------------------------------------
+// one element of Adam / AdamW, every operation rounded on its own
+
+template <bool L2>
+__device__ __forceinline__ void adam1(float acc, float& p, float& m, float& v, const StepScalars& s) {
+  float g = acc * s.gs;
+  if (L2) g = g + s.w * p;
+  m = s.b1 * m + s.c1 * g;
+  v = s.b2 * v + s.c2 * (g * g);
+  const float den = sqrtf(v) / s.bc + s.e;
+  if (!L2) p = p * s.dec;
+  p = p - s.ss * (m / den);
+}
+
+// ---------------------------------------------------------------------------------------------
+// fused step: replica sum -> Adam/AdamW on master/m/v -> 16-bit cast into the rank's slot
+
+template <int RDT, int ODT, bool L2, bool VEC, int RFIX>
+__global__ __launch_bounds__(kBlock) void k_adam_step(RepPtrs reps, int nrep, uint64_t n,
+                                                      StepScalars sc, float* __restrict__ P,
+                                                      float* __restrict__ M, float* __restrict__ V,
+                                                      void* __restrict__ out,
+                                                      const int32_t* __restrict__ skip) {
+  if (skip != nullptr && *skip != 0) return;
+  constexpr int SUB = ZERO_ADAM_SUB;
+  constexpr uint64_t kTile = (uint64_t)kBlock * 4 * SUB;
+  const uint64_t ntiles = (n + kTile - 1) / kTile;
+  for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const uint64_t base = t * kTile;
+    if (VEC && base + kTile <= n) {
+      uint64_t idx[SUB];
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) idx[u] = base + (uint64_t)u * (kBlock * 4) + threadIdx.x * 4u;
+      f32x4 p[SUB], m[SUB], v[SUB], acc[SUB];
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        p[u] = ld(reinterpret_cast<const f32x4*>(P + idx[u]));
+        m[u] = ld(reinterpret_cast<const f32x4*>(M + idx[u]));
+        v[u] = ld(reinterpret_cast<const f32x4*>(V + idx[u]));
+      }
+      sum_reps4<RDT, RFIX, SUB>(reps, nrep, idx, acc);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float pq = p[u][q], mq = m[u][q], vq = v[u][q];
+          adam1<L2>(acc[u][q], pq, mq, vq, sc);
+          p[u][q] = pq;
+          m[u][q] = mq;
+          v[u][q] = vq;
+        }
+        st(reinterpret_cast<f32x4*>(P + idx[u]), p[u]);
+        st(reinterpret_cast<f32x4*>(M + idx[u]), m[u]);
+        st(reinterpret_cast<f32x4*>(V + idx[u]), v[u]);
+        if constexpr (ODT != ZERO_F32) {
+          u32x2 o;
+          o.x = to_out<ODT>(p[u].x) | (to_out<ODT>(p[u].y) << 16);
+          o.y = to_out<ODT>(p[u].z) | (to_out<ODT>(p[u].w) << 16);
+          st(reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx[u]), o);
+        }
+      }
+    } else {
+      const int R = RFIX ? RFIX : nrep;
+      for (int j = 0; j < (int)(kTile / kBlock); ++j) {
+        const uint64_t i = base + (uint64_t)j * kBlock + threadIdx.x;
+        if (i < n) {
+          const float a = sum_reps1<RDT>(reps, R, i);
+          float p = P[i], m = M[i], v = V[i];
+          adam1<L2>(a, p, m, v, sc);
+          P[i] = p;
+          M[i] = m;
+          V[i] = v;
+          if constexpr (ODT != ZERO_F32) static_cast<uint16_t*>(out)[i] = (uint16_t)to_out<ODT>(p);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// reduce pass: replica sum -> fp32 gradient, non-finite flag, fp64 squared-norm partials
+//
+// The grid is a function of n alone (min(ZERO_SQ_PARTIALS, tiles)), each thread adds its own
+// elements in a fixed order, and the block sum uses a fixed butterfly, so the partials are
+// bit-reproducible. No atomics: the flag is only ever set to 1 by plain stores.
+
+__device__ __forceinline__ double block_sum(double x, double* lds) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) lds[wave] = x;
+  __syncthreads();
+  double s = 0.0;
+  if (threadIdx.x == 0) {
+    s = lds[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) s += lds[w];
+  }
+  return s;  // meaningful in thread 0 only
+}
+
+__device__ __forceinline__ bool nonfinite(float x) {
+  return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u;
+}
+
+template <int RDT, bool VEC, int RFIX>
+__global__ __launch_bounds__(kBlock) void k_reduce(RepPtrs reps, int nrep, uint64_t n,
+                                                   float* __restrict__ G, int32_t* __restrict__ flag,
+                                                   double* __restrict__ partials, double sq_scale) {
+  constexpr int SUB = ZERO_REDUCE_SUB;
+  constexpr uint64_t kTile = (uint64_t)kBlock * 4 * SUB;
+  __shared__ double lds[kWaves];
+  const uint64_t ntiles = (n + kTile - 1) / kTile;
+  double sq = 0.0;
+  bool bad = false;
+  for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const uint64_t base = t * kTile;
+    if (VEC && base + kTile <= n) {
+      uint64_t idx[SUB];
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) idx[u] = base + (uint64_t)u * (kBlock * 4) + threadIdx.x * 4u;
+      f32x4 acc[SUB];
+      sum_reps4<RDT, RFIX, SUB>(reps, nrep, idx, acc);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        if (G != nullptr) st(reinterpret_cast<f32x4*>(G + idx[u]), acc[u]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bad |= nonfinite(acc[u][q]);
+          const double d = (double)acc[u][q] * sq_scale;
+          sq += d * d;
+        }
+      }
+    } else {
+      const int R = RFIX ? RFIX : nrep;
+      for (int j = 0; j < (int)(kTile / kBlock); ++j) {
+        const uint64_t i = base + (uint64_t)j * kBlock + threadIdx.x;
+        if (i < n) {
+          const float a = sum_reps1<RDT>(reps, R, i);
+          if (G != nullptr) G[i] = a;
+          bad |= nonfinite(a);
+          const double d = (double)a * sq_scale;
+          sq += d * d;
+        }
+      }
+    }
+  }
+  if (flag != nullptr) {
+    if (__syncthreads_or(bad) && threadIdx.x == 0) *flag = 1;
+  }
+  if (partials != nullptr) {
+    const double s = block_sum(sq, lds);
+    if (threadIdx.x == 0) partials[blockIdx.x] = s;
+    if (blockIdx.x == 0)
+      for (uint32_t i = gridDim.x + threadIdx.x; i < ZERO_SQ_PARTIALS; i += kBlock) partials[i] = 0.0;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_zero_partials(double* __restrict__ partials) {
+  for (uint32_t i = threadIdx.x; i < ZERO_SQ_PARTIALS; i += kBlock) partials[i] = 0.0;
+}
+
+__global__ __launch_bounds__(kBlock) void k_sq_finalize(const double* __restrict__ partials,
+                                                        double* __restrict__ out) {
+  __shared__ double lds[kWaves];
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < ZERO_SQ_PARTIALS / kBlock; ++j) s += partials[threadIdx.x + j * kBlock];
+  s = block_sum(s, lds);
+  if (threadIdx.x == 0) *out = s;
+}
+
+// ---------------------------------------------------------------------------------------------
+// host side
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];  // per-device compute-unit count, filled on first use
+
+zero_status cu_count(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return zero::fail(ZERO_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return zero::fail(ZERO_E_UNSUPPORTED, "device index %d", dev);
+  if (g_cu_count[dev] == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+      return zero::fail(ZERO_E_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    g_cu_count[dev] = cus > 0 ? cus : 1;
+  }
+  *out = g_cu_count[dev];
+  return ZERO_OK;
+}
+
+zero_status launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return zero::fail(ZERO_E_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return zero::ok();
+}
+
+zero_status check_src(const char* fn, const zero_grad_src* src, uint64_t n) {
+  if (!src || !src->ptrs) return zero::fail(ZERO_E_INVAL, "%s: gradient source is NULL", fn);
+  if (src->count == 0 || src->count > ZERO_MAX_REPLICAS)
+    return zero::fail(ZERO_E_INVAL, "%s: replica count %u outside 1..%d", fn, src->count,
+                      ZERO_MAX_REPLICAS);
+  if (!zero::dtype_valid(src->dtype))
+    return zero::fail(ZERO_E_INVAL, "%s: unknown replica dtype %d", fn, src->dtype);
+  for (uint32_t k = 0; k < src->count; ++k)
+    if (!src->ptrs[k]) return zero::fail(ZERO_E_INVAL, "%s: replica %u is NULL", fn, k);
+  if (n > UINT64_MAX / 8) return zero::fail(ZERO_E_OVERFLOW, "%s: n = %llu too large", fn,
+                                            (unsigned long long)n);
+  return ZERO_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool src_aligned(const zero_grad_src* src) {
+  const uintptr_t a = 4u * zero::dtype_bytes(src->dtype);
+  for (uint32_t k = 0; k < src->count; ++k)
+    if (!aligned(src->ptrs[k], a)) return false;
+  return true;
+}
+
+RepPtrs rep_ptrs(const zero_grad_src* src) {
+  RepPtrs r{};
+  for (uint32_t k = 0; k < src->count; ++k) r.p[k] = src->ptrs[k];
+  return r;
+}
+
+// ----- Adam dispatch
+
+struct AdamArgs {
+  RepPtrs reps;
+  int nrep;
+  uint64_t n;
+  StepScalars sc;
+  float *P, *M, *V;
+  void* out;
+  const int32_t* skip;
+  dim3 grid;
+  hipStream_t stream;
+};
+
+template <int RDT, int ODT, bool L2, bool VEC, int RFIX>
+void launch_adam(const AdamArgs& a) {
+  hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, VEC, RFIX>), a.grid, dim3(kBlock), 0, a.stream,
+                     a.reps, a.nrep, a.n, a.sc, a.P, a.M, a.V, a.out, a.skip);
+}
+
+template <int RDT, int ODT, bool L2, bool VEC>
+void adam_by_r(const AdamArgs& a) {
+  if constexpr (!VEC) {
+    launch_adam<RDT, ODT, L2, false, 0>(a);
+  } else {
+    switch (a.nrep) {
+      case 1: launch_adam<RDT, ODT, L2, true, 1>(a); break;
+      case 8: launch_adam<RDT, ODT, L2, true, 8>(a); break;
+      case 16: launch_adam<RDT, ODT, L2, true, 16>(a); break;
+      case 64: launch_adam<RDT, ODT, L2, true, 64>(a); break;
+      default: launch_adam<RDT, ODT, L2, true, 0>(a); break;
+    }
+  }
+}
+
+template <int RDT, int ODT, bool L2>
+void adam_by_vec(const AdamArgs& a, bool vec) {
+  if (vec) adam_by_r<RDT, ODT, L2, true>(a);
+  else adam_by_r<RDT, ODT, L2, false>(a);
+}
+
+template <int RDT, int ODT>
+void adam_by_l2(const AdamArgs& a, bool l2, bool vec) {
+  if (l2) adam_by_vec<RDT, ODT, true>(a, vec);
+  else adam_by_vec<RDT, ODT, false>(a, vec);
+}
+
+template <int RDT>
+void adam_by_out(const AdamArgs& a, int odt, bool l2, bool vec) {
+  if (odt == ZERO_BF16) adam_by_l2<RDT, ZERO_BF16>(a, l2, vec);
+  else if (odt == ZERO_F16) adam_by_l2<RDT, ZERO_F16>(a, l2, vec);
+  else adam_by_l2<RDT, ZERO_F32>(a, l2, vec);  // ZERO_F32 here means "no 16-bit output"
+}
+
+// ----- reduce dispatch
+
+struct ReduceArgs {
+  RepPtrs reps;
+  int nrep;
+  uint64_t n;
+  float* G;
+  int32_t* flag;
+  double* partials;
+  double sq_scale;
+  dim3 grid;
+  hipStream_t stream;
+};
+
+template <int RDT, bool VEC, int RFIX>
+void launch_reduce(const ReduceArgs& a) {
+  hipLaunchKernelGGL((k_reduce<RDT, VEC, RFIX>), a.grid, dim3(kBlock), 0, a.stream, a.reps, a.nrep,
+                     a.n, a.G, a.flag, a.partials, a.sq_scale);
+}
+
+template <int RDT>
+void reduce_by_r(const ReduceArgs& a, bool vec) {
+  if (!vec) return launch_reduce<RDT, false, 0>(a);
+  switch (a.nrep) {
+    case 1: launch_reduce<RDT, true, 1>(a); break;
+    case 8: launch_reduce<RDT, true, 8>(a); break;
+    case 16: launch_reduce<RDT, true, 16>(a); break;
+    case 64: launch_reduce<RDT, true, 64>(a); break;
+    default: launch_reduce<RDT, true, 0>(a); break;
+  }
+}
+
+constexpr uint64_t kReduceTile = (uint64_t)kBlock * 4 * ZERO_REDUCE_SUB;
+constexpr uint64_t kAdamTile = (uint64_t)kBlock * 4 * ZERO_ADAM_SUB;
+
+dim3 reduce_grid(uint64_t n) {
+  const uint64_t tiles = (n + kReduceTile - 1) / kReduceTile;
+  return dim3((unsigned)(tiles < ZERO_SQ_PARTIALS ? (tiles ? tiles : 1) : ZERO_SQ_PARTIALS));
+}
+
+zero_status reduce_impl(const zero_grad_src* src, uint64_t n, float* G, int32_t* flag,
+                        double* partials, double sq_scale, hipStream_t stream, const char* what) {
+  if (n == 0) {
+    if (partials != nullptr) {
+      hipLaunchKernelGGL(k_zero_partials, dim3(1), dim3(kBlock), 0, stream, partials);
+      return launched(what);
+    }
+    return zero::ok();
+  }
+  ReduceArgs a{rep_ptrs(src), (int)src->count, n, G, flag, partials, sq_scale, reduce_grid(n), stream};
+  const bool vec = src_aligned(src) && (G == nullptr || aligned(G, 16));
+  (void)hipGetLastError();
+  switch (src->dtype) {
+    case ZERO_F32: reduce_by_r<ZERO_F32>(a, vec); break;
+    case ZERO_F16: reduce_by_r<ZERO_F16>(a, vec); break;
+    default: reduce_by_r<ZERO_BF16>(a, vec); break;
+  }
+  return launched(what);
+}
+
+}  // namespace
+
+extern "C" {
+
+zero_status zero_reduce_shard(const zero_grad_src* src, uint64_t n, float* out_grad,
+                              int32_t* d_nonfinite, double* d_sq_partials, double sq_scale,
+                              void* stream) {
+  const char* fn = "zero_reduce_shard";
+  zero_status s = check_src(fn, src, n);
+  if (s != ZERO_OK) return s;
+  if (!out_grad && !d_nonfinite && !d_sq_partials)
+    return zero::fail(ZERO_E_INVAL, "%s: no output requested", fn);
+  const uint64_t rb = n * zero::dtype_bytes(src->dtype);
+  if (out_grad) {
+    for (uint32_t k = 0; k < src->count; ++k)
+      if (zero::overlaps(out_grad, n * 4, src->ptrs[k], rb))
+        return zero::fail(ZERO_E_INVAL, "%s: out_grad overlaps replica %u", fn, k);
+  }
+  if (d_sq_partials && out_grad &&
+      zero::overlaps(d_sq_partials, ZERO_SQ_PARTIALS * 8, out_grad, n * 4))
+    return zero::fail(ZERO_E_INVAL, "%s: partials overlap out_grad", fn);
+  return reduce_impl(src, n, out_grad, d_nonfinite, d_sq_partials, sq_scale,
+                     static_cast<hipStream_t>(stream), fn);
+}
+
+zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, double* d_partials,
+                              double* d_out, void* stream) {
+  const char* fn = "zero_shard_sqnorm";
+  if (!d_partials || !d_out) return zero::fail(ZERO_E_INVAL, "%s: partials or out is NULL", fn);
+  if (zero::overlaps(d_partials, ZERO_SQ_PARTIALS * 8, d_out, 8))
+    return zero::fail(ZERO_E_INVAL, "%s: out overlaps the partials", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d_grad != nullptr) {
+    const void* ptrs[1] = {d_grad};
+    const zero_grad_src src{ptrs, 1, ZERO_F32};
+    zero_status s = check_src(fn, &src, n);
+    if (s != ZERO_OK) return s;
+    if (zero::overlaps(d_partials, ZERO_SQ_PARTIALS * 8, d_grad, n * 4))
+      return zero::fail(ZERO_E_INVAL, "%s: partials overlap the gradient", fn);
+    s = reduce_impl(&src, n, nullptr, nullptr, d_partials, sq_scale, st, fn);
+    if (s != ZERO_OK) return s;
+  }
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_sq_finalize, dim3(1), dim3(kBlock), 0, st, d_partials, d_out);
+  return launched(fn);
+}
+
+zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float grad_scale,
+                                 float* master, float* m, float* v, const zero_adam_hparams* hp,
+                                 void* out_param, int32_t out_dtype, const int32_t* d_skip,
+                                 void* stream) {
+  const char* fn = "zero_adam_shard_step";
+  zero_status s = check_src(fn, src, n);
+  if (s != ZERO_OK) return s;
+  if (!master || !m || !v) return zero::fail(ZERO_E_INVAL, "%s: master, m or v is NULL", fn);
+  zero_adam_scalars k;
+  s = zero_adam_derive(hp, &k);
+  if (s != ZERO_OK) return s;
+  if (out_param) {
+    if (out_dtype == ZERO_F32)
+      return zero::fail(ZERO_E_UNSUPPORTED, "%s: fp32 parameter output is not supported", fn);
+    if (out_dtype != ZERO_BF16 && out_dtype != ZERO_F16)
+      return zero::fail(ZERO_E_INVAL, "%s: unknown out dtype %d", fn, out_dtype);
+  }
+  const uint64_t sb = n * 4, ob = out_param ? n * 2 : 0, rb = n * zero::dtype_bytes(src->dtype);
+  const void* own[4] = {master, m, v, out_param};
+  const uint64_t own_b[4] = {sb, sb, sb, ob};
+  for (int x = 0; x < 4; ++x) {
+    for (int y = x + 1; y < 4; ++y)
+      if (zero::overlaps(own[x], own_b[x], own[y], own_b[y]))
+        return zero::fail(ZERO_E_INVAL, "%s: output arrays %d and %d overlap", fn, x, y);
+    for (uint32_t r = 0; r < src->count; ++r)
+      if (zero::overlaps(own[x], own_b[x], src->ptrs[r], rb))
+        return zero::fail(ZERO_E_INVAL, "%s: output array %d overlaps replica %u", fn, x, r);
+  }
+  if (n == 0) return zero::ok();
+
+  int cus = 0;
+  s = cu_count(&cus);
+  if (s != ZERO_OK) return s;
+  const uint64_t tiles = (n + kAdamTile - 1) / kAdamTile;
+  uint64_t grid = ZERO_ADAM_BLOCKS_PER_CU > 0 ? (uint64_t)cus * ZERO_ADAM_BLOCKS_PER_CU : tiles;
+  if (grid > tiles) grid = tiles;
+  if (grid > (1u << 24)) grid = 1u << 24;  // keeps grid*block below 2^32 work-items
+
+  const bool vec = src_aligned(src) && aligned(master, 16) && aligned(m, 16) && aligned(v, 16) &&
+                   (out_param == nullptr || aligned(out_param, 8));
+  AdamArgs a{rep_ptrs(src), (int)src->count, n,
+             StepScalars{grad_scale, k.b1, k.b2, k.c1, k.c2, k.ss, k.bc, k.e, k.dec, k.w},
+             master, m, v, out_param, d_skip, dim3((unsigned)grid),
+             static_cast<hipStream_t>(stream)};
+  const int odt = out_param ? out_dtype : ZERO_F32;
+  const bool l2 = hp->wd_mode == ZERO_ADAM_L2;
+  (void)hipGetLastError();
+  switch (src->dtype) {
+    case ZERO_F32: adam_by_out<ZERO_F32>(a, odt, l2, vec); break;
+    case ZERO_F16: adam_by_out<ZERO_F16>(a, odt, l2, vec); break;
+    default: adam_by_out<ZERO_BF16>(a, odt, l2, vec); break;
+  }
+  return launched(fn);
+}
+
+}  // extern "C"

@@ -1,11 +1,13 @@
 // gfx950 kernels of the per-rank sharded optimizer step and their C-ABI launchers.
 //
 // Everything here is HBM-bound elementwise streaming (about 0.5 flop per byte), so nothing is
-// shaped for MFMA. Each block owns contiguous tiles of kTile elements; inside a tile a thread owns
-// kSub groups of 4 consecutive elements spaced kBlock*4 apart, so every load instruction of a
-// wave covers one contiguous 1 KiB (fp32) or 512 B (16-bit) run. Full tiles whose arrays are all
-// 16-byte aligned take that vector path; the ragged last tile and misaligned arrays take a
-// per-element path with the same arithmetic.
+// shaped for MFMA. A tile is SUB groups of 4 consecutive elements per thread, the groups spaced
+// block*4 elements apart, so every load instruction of a wave covers one contiguous 1 KiB (fp32)
+// or 512 B (16-bit) run. Loads and stores are non-temporal: every byte is touched once per step.
+// The Adam kernel runs one single-wave tile per block over the aligned whole tiles of the shard;
+// a separate per-element kernel takes the ragged end and arrays that are not 16-byte aligned.
+// Measured on MI355X, one-wave blocks with 2 groups per lane moved this 15-stream read/write mix
+// faster than 128- or 256-thread blocks and than grid-stride (persistent) launches.
 //
 // Arithmetic is fp32 with every operation rounded on its own: the library is built with
 // -ffp-contract=off and HIP's correctly rounded fp32 division and square root, so the results
@@ -21,17 +23,26 @@
 #ifndef ZERO_REDUCE_SUB
 #define ZERO_REDUCE_SUB 2          // same for the reduce / squared-norm kernel
 #endif
-#ifndef ZERO_ADAM_BLOCKS_PER_CU
-#define ZERO_ADAM_BLOCKS_PER_CU 0  // 0: one tile per block; k > 0: grid-stride over k*CUs blocks
-#endif
 #ifndef ZERO_NT
 #define ZERO_NT 1                  // streaming (non-temporal) loads and stores: data is touched once
+#endif
+#ifndef ZERO_ADAM_BLOCK
+#define ZERO_ADAM_BLOCK 64         // threads per block of the Adam kernel (one wave)
+#endif
+#ifndef ZERO_ADAM_WAVES
+#define ZERO_ADAM_WAVES 0          // > 0: ask for at least this many waves per SIMD (register cap)
+#endif
+#if ZERO_ADAM_WAVES > 0
+#define ZERO_ADAM_WAVES_ATTR __attribute__((amdgpu_waves_per_eu(ZERO_ADAM_WAVES)))
+#else
+#define ZERO_ADAM_WAVES_ATTR
 #endif
 
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = 256;            // reduce / squared-norm kernels
 constexpr int kWaves = kBlock / 64;
+constexpr int kAdamBlock = ZERO_ADAM_BLOCK;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -170,66 +181,76 @@ __device__ __forceinline__ void adam1(float acc, float& p, float& m, float& v, c
 
 // ---------------------------------------------------------------------------------------------
 // fused step: replica sum -> Adam/AdamW on master/m/v -> 16-bit cast into the rank's slot
+//
+// Two kernels share the arithmetic. k_adam_step covers whole tiles of arrays that are all 16-byte
+// aligned (8-byte for 16-bit arrays) with vector loads and stores, one tile per block; it holds no
+// per-element path, so its register budget stays small and more waves fit on a SIMD. k_adam_tail
+// covers any other element range (the ragged end of a shard, or a shard whose arrays are not
+// aligned) one element per thread.
 
-template <int RDT, int ODT, bool L2, bool VEC, int RFIX>
-__global__ __launch_bounds__(kBlock) void k_adam_step(RepPtrs reps, int nrep, uint64_t n,
-                                                      StepScalars sc, float* __restrict__ P,
-                                                      float* __restrict__ M, float* __restrict__ V,
-                                                      void* __restrict__ out,
+template <int RDT, int ODT, bool L2, int RFIX, bool SKIP>
+__global__ __launch_bounds__(kAdamBlock) ZERO_ADAM_WAVES_ATTR void k_adam_step(
+    RepPtrs reps, int nrep, uint64_t first_tile, StepScalars sc, float* __restrict__ P,
+    float* __restrict__ M, float* __restrict__ V, void* __restrict__ out,
+    const int32_t* __restrict__ skip) {
+  // One tile per block and the grid is exactly the tile count: no loop bound and no per-block
+  // bound check to wait for, so a block's first loads issue right after its arguments arrive.
+  if constexpr (SKIP) {
+    if (*skip != 0) return;
+  }
+  constexpr int SUB = ZERO_ADAM_SUB;
+  constexpr uint64_t kTile = (uint64_t)kAdamBlock * 4 * SUB;
+  const uint64_t base = (first_tile + blockIdx.x) * kTile;
+  uint64_t idx[SUB];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) idx[u] = base + (uint64_t)u * (kAdamBlock * 4) + threadIdx.x * 4u;
+  f32x4 p[SUB], m[SUB], v[SUB], acc[SUB];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    p[u] = ld(reinterpret_cast<const f32x4*>(P + idx[u]));
+    m[u] = ld(reinterpret_cast<const f32x4*>(M + idx[u]));
+    v[u] = ld(reinterpret_cast<const f32x4*>(V + idx[u]));
+  }
+  sum_reps4<RDT, RFIX, SUB>(reps, nrep, idx, acc);
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float pq = p[u][q], mq = m[u][q], vq = v[u][q];
+      adam1<L2>(acc[u][q], pq, mq, vq, sc);
+      p[u][q] = pq;
+      m[u][q] = mq;
+      v[u][q] = vq;
+    }
+    st(reinterpret_cast<f32x4*>(P + idx[u]), p[u]);
+    st(reinterpret_cast<f32x4*>(M + idx[u]), m[u]);
+    st(reinterpret_cast<f32x4*>(V + idx[u]), v[u]);
+    if constexpr (ODT != ZERO_F32) {
+      u32x2 o;
+      o.x = to_out<ODT>(p[u].x) | (to_out<ODT>(p[u].y) << 16);
+      o.y = to_out<ODT>(p[u].z) | (to_out<ODT>(p[u].w) << 16);
+      st(reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx[u]), o);
+    }
+  }
+}
+
+// elements [begin, n), one per thread per grid-stride iteration, any alignment
+template <int RDT, int ODT, bool L2>
+__global__ __launch_bounds__(kBlock) void k_adam_tail(RepPtrs reps, int nrep, uint64_t begin,
+                                                      uint64_t n, StepScalars sc,
+                                                      float* __restrict__ P, float* __restrict__ M,
+                                                      float* __restrict__ V, void* __restrict__ out,
                                                       const int32_t* __restrict__ skip) {
   if (skip != nullptr && *skip != 0) return;
-  constexpr int SUB = ZERO_ADAM_SUB;
-  constexpr uint64_t kTile = (uint64_t)kBlock * 4 * SUB;
-  const uint64_t ntiles = (n + kTile - 1) / kTile;
-  for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const uint64_t base = t * kTile;
-    if (VEC && base + kTile <= n) {
-      uint64_t idx[SUB];
-#pragma unroll
-      for (int u = 0; u < SUB; ++u) idx[u] = base + (uint64_t)u * (kBlock * 4) + threadIdx.x * 4u;
-      f32x4 p[SUB], m[SUB], v[SUB], acc[SUB];
-#pragma unroll
-      for (int u = 0; u < SUB; ++u) {
-        p[u] = ld(reinterpret_cast<const f32x4*>(P + idx[u]));
-        m[u] = ld(reinterpret_cast<const f32x4*>(M + idx[u]));
-        v[u] = ld(reinterpret_cast<const f32x4*>(V + idx[u]));
-      }
-      sum_reps4<RDT, RFIX, SUB>(reps, nrep, idx, acc);
-#pragma unroll
-      for (int u = 0; u < SUB; ++u) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float pq = p[u][q], mq = m[u][q], vq = v[u][q];
-          adam1<L2>(acc[u][q], pq, mq, vq, sc);
-          p[u][q] = pq;
-          m[u][q] = mq;
-          v[u][q] = vq;
-        }
-        st(reinterpret_cast<f32x4*>(P + idx[u]), p[u]);
-        st(reinterpret_cast<f32x4*>(M + idx[u]), m[u]);
-        st(reinterpret_cast<f32x4*>(V + idx[u]), v[u]);
-        if constexpr (ODT != ZERO_F32) {
-          u32x2 o;
-          o.x = to_out<ODT>(p[u].x) | (to_out<ODT>(p[u].y) << 16);
-          o.y = to_out<ODT>(p[u].z) | (to_out<ODT>(p[u].w) << 16);
-          st(reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx[u]), o);
-        }
-      }
-    } else {
-      const int R = RFIX ? RFIX : nrep;
-      for (int j = 0; j < (int)(kTile / kBlock); ++j) {
-        const uint64_t i = base + (uint64_t)j * kBlock + threadIdx.x;
-        if (i < n) {
-          const float a = sum_reps1<RDT>(reps, R, i);
-          float p = P[i], m = M[i], v = V[i];
-          adam1<L2>(a, p, m, v, sc);
-          P[i] = p;
-          M[i] = m;
-          V[i] = v;
-          if constexpr (ODT != ZERO_F32) static_cast<uint16_t*>(out)[i] = (uint16_t)to_out<ODT>(p);
-        }
-      }
-    }
+  for (uint64_t i = begin + (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+       i += (uint64_t)gridDim.x * kBlock) {
+    const float a = sum_reps1<RDT>(reps, nrep, i);
+    float p = P[i], m = M[i], v = V[i];
+    adam1<L2>(a, p, m, v, sc);
+    P[i] = p;
+    M[i] = m;
+    V[i] = v;
+    if constexpr (ODT != ZERO_F32) static_cast<uint16_t*>(out)[i] = (uint16_t)to_out<ODT>(p);
   }
 }
 
@@ -385,56 +406,67 @@ RepPtrs rep_ptrs(const zero_grad_src* src) {
 
 // ----- Adam dispatch
 
+constexpr uint64_t kReduceTile = (uint64_t)kBlock * 4 * ZERO_REDUCE_SUB;
+constexpr uint64_t kAdamTile = (uint64_t)kAdamBlock * 4 * ZERO_ADAM_SUB;
+constexpr uint64_t kMaxGrid = 1u << 24;  // blocks per Adam launch; keeps grid * block below 2^32
+
 struct AdamArgs {
   RepPtrs reps;
   int nrep;
+  uint64_t ntiles;      // whole vector tiles (k_adam_step), from element 0
+  uint64_t tail_begin;  // first element of the per-element range (k_adam_tail)
   uint64_t n;
   StepScalars sc;
   float *P, *M, *V;
   void* out;
   const int32_t* skip;
-  dim3 grid;
+  unsigned tail_grid;
   hipStream_t stream;
 };
 
-template <int RDT, int ODT, bool L2, bool VEC, int RFIX>
+template <int RDT, int ODT, bool L2, int RFIX>
 void launch_adam(const AdamArgs& a) {
-  hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, VEC, RFIX>), a.grid, dim3(kBlock), 0, a.stream,
-                     a.reps, a.nrep, a.n, a.sc, a.P, a.M, a.V, a.out, a.skip);
-}
-
-template <int RDT, int ODT, bool L2, bool VEC>
-void adam_by_r(const AdamArgs& a) {
-  if constexpr (!VEC) {
-    launch_adam<RDT, ODT, L2, false, 0>(a);
-  } else {
-    switch (a.nrep) {
-      case 1: launch_adam<RDT, ODT, L2, true, 1>(a); break;
-      case 8: launch_adam<RDT, ODT, L2, true, 8>(a); break;
-      case 16: launch_adam<RDT, ODT, L2, true, 16>(a); break;
-      case 64: launch_adam<RDT, ODT, L2, true, 64>(a); break;
-      default: launch_adam<RDT, ODT, L2, true, 0>(a); break;
-    }
+  // grids of at most kMaxGrid tiles, each told where its first tile is
+  for (uint64_t t0 = 0; t0 < a.ntiles; t0 += kMaxGrid) {
+    const uint64_t g = a.ntiles - t0 < kMaxGrid ? a.ntiles - t0 : kMaxGrid;
+    if (a.skip != nullptr)
+      hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, true>), dim3((unsigned)g),
+                         dim3(kAdamBlock), 0, a.stream, a.reps, a.nrep, t0, a.sc, a.P, a.M, a.V,
+                         a.out, a.skip);
+    else
+      hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, false>), dim3((unsigned)g),
+                         dim3(kAdamBlock), 0, a.stream, a.reps, a.nrep, t0, a.sc, a.P, a.M, a.V,
+                         a.out, a.skip);
   }
 }
 
 template <int RDT, int ODT, bool L2>
-void adam_by_vec(const AdamArgs& a, bool vec) {
-  if (vec) adam_by_r<RDT, ODT, L2, true>(a);
-  else adam_by_r<RDT, ODT, L2, false>(a);
+void adam_kernels(const AdamArgs& a) {
+  if (a.ntiles > 0) {
+    switch (a.nrep) {
+      case 1: launch_adam<RDT, ODT, L2, 1>(a); break;
+      case 8: launch_adam<RDT, ODT, L2, 8>(a); break;
+      case 16: launch_adam<RDT, ODT, L2, 16>(a); break;
+      case 64: launch_adam<RDT, ODT, L2, 64>(a); break;
+      default: launch_adam<RDT, ODT, L2, 0>(a); break;
+    }
+  }
+  if (a.tail_begin < a.n)
+    hipLaunchKernelGGL((k_adam_tail<RDT, ODT, L2>), dim3(a.tail_grid), dim3(kBlock), 0, a.stream,
+                       a.reps, a.nrep, a.tail_begin, a.n, a.sc, a.P, a.M, a.V, a.out, a.skip);
 }
 
 template <int RDT, int ODT>
-void adam_by_l2(const AdamArgs& a, bool l2, bool vec) {
-  if (l2) adam_by_vec<RDT, ODT, true>(a, vec);
-  else adam_by_vec<RDT, ODT, false>(a, vec);
+void adam_by_l2(const AdamArgs& a, bool l2) {
+  if (l2) adam_kernels<RDT, ODT, true>(a);
+  else adam_kernels<RDT, ODT, false>(a);
 }
 
 template <int RDT>
-void adam_by_out(const AdamArgs& a, int odt, bool l2, bool vec) {
-  if (odt == ZERO_BF16) adam_by_l2<RDT, ZERO_BF16>(a, l2, vec);
-  else if (odt == ZERO_F16) adam_by_l2<RDT, ZERO_F16>(a, l2, vec);
-  else adam_by_l2<RDT, ZERO_F32>(a, l2, vec);  // ZERO_F32 here means "no 16-bit output"
+void adam_by_out(const AdamArgs& a, int odt, bool l2) {
+  if (odt == ZERO_BF16) adam_by_l2<RDT, ZERO_BF16>(a, l2);
+  else if (odt == ZERO_F16) adam_by_l2<RDT, ZERO_F16>(a, l2);
+  else adam_by_l2<RDT, ZERO_F32>(a, l2);  // ZERO_F32 here means "no 16-bit output"
 }
 
 // ----- reduce dispatch
@@ -469,8 +501,6 @@ void reduce_by_r(const ReduceArgs& a, bool vec) {
   }
 }
 
-constexpr uint64_t kReduceTile = (uint64_t)kBlock * 4 * ZERO_REDUCE_SUB;
-constexpr uint64_t kAdamTile = (uint64_t)kBlock * 4 * ZERO_ADAM_SUB;
 
 dim3 reduce_grid(uint64_t n) {
   const uint64_t tiles = (n + kReduceTile - 1) / kReduceTile;
@@ -577,24 +607,23 @@ zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float gra
   int cus = 0;
   s = cu_count(&cus);
   if (s != ZERO_OK) return s;
-  const uint64_t tiles = (n + kAdamTile - 1) / kAdamTile;
-  uint64_t grid = ZERO_ADAM_BLOCKS_PER_CU > 0 ? (uint64_t)cus * ZERO_ADAM_BLOCKS_PER_CU : tiles;
-  if (grid > tiles) grid = tiles;
-  if (grid > (1u << 24)) grid = 1u << 24;  // keeps grid*block below 2^32 work-items
-
   const bool vec = src_aligned(src) && aligned(master, 16) && aligned(m, 16) && aligned(v, 16) &&
                    (out_param == nullptr || aligned(out_param, 8));
-  AdamArgs a{rep_ptrs(src), (int)src->count, n,
+  const uint64_t ntiles = vec ? n / kAdamTile : 0;
+  const uint64_t tail_begin = ntiles * kAdamTile, tail_n = n - tail_begin;
+  uint64_t tail_grid = (tail_n + kBlock - 1) / kBlock;
+  if (tail_grid > (uint64_t)cus * 8) tail_grid = (uint64_t)cus * 8;
+  AdamArgs a{rep_ptrs(src), (int)src->count, ntiles, tail_begin, n,
              StepScalars{grad_scale, k.b1, k.b2, k.c1, k.c2, k.ss, k.bc, k.e, k.dec, k.w},
-             master, m, v, out_param, d_skip, dim3((unsigned)grid),
+             master, m, v, out_param, d_skip, (unsigned)tail_grid,
              static_cast<hipStream_t>(stream)};
   const int odt = out_param ? out_dtype : ZERO_F32;
   const bool l2 = hp->wd_mode == ZERO_ADAM_L2;
   (void)hipGetLastError();
   switch (src->dtype) {
-    case ZERO_F32: adam_by_out<ZERO_F32>(a, odt, l2, vec); break;
-    case ZERO_F16: adam_by_out<ZERO_F16>(a, odt, l2, vec); break;
-    default: adam_by_out<ZERO_BF16>(a, odt, l2, vec); break;
+    case ZERO_F32: adam_by_out<ZERO_F32>(a, odt, l2); break;
+    case ZERO_F16: adam_by_out<ZERO_F16>(a, odt, l2); break;
+    default: adam_by_out<ZERO_BF16>(a, odt, l2); break;
   }
   return launched(fn);
 }

@@ -268,7 +268,7 @@ def setup(name: str):
     if name == "llama13b":
         state["g"] = torch.empty(S, device=dev)
         state["flag"] = torch.zeros(1, dtype=torch.int32, device=dev)
-        state["parts"] = torch.empty(Z.ZERO_SQ_PARTIALS, dtype=torch.float64, device=dev)
+        state["parts"] = torch.empty(Z.zero_sq_partials_len(S), dtype=torch.float64, device=dev)
         state["sq"] = torch.empty(1, dtype=torch.float64, device=dev)
     torch.cuda.synchronize()
     return state

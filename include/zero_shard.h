@@ -34,7 +34,6 @@ extern "C" {
 #endif
 
 #define ZERO_MAX_REPLICAS 64   /* gradient replicas one call can sum */
-#define ZERO_SQ_PARTIALS 2048  /* fp64 partial sums written by the squared-norm passes */
 
 typedef enum {
   ZERO_OK = 0,
@@ -115,25 +114,33 @@ zero_status zero_stage_bytes(const zero_plan* p, uint32_t stage, uint32_t param_
  * non-finite or negative lr/eps/wd, unknown wd_mode -> ZERO_E_INVAL. */
 zero_status zero_adam_derive(const zero_adam_hparams* hp, zero_adam_scalars* out);
 
+/* Length, in doubles, of the squared-norm partials buffer for a shard of n elements:
+ * ceil(n / 512) per-tile partials followed by 1024 second-level slots. Host only; never fails. */
+uint64_t zero_sq_partials_len(uint64_t n);
+
 /* Reduction half of the gradient reduce-scatter, done over local replicas (P1 section 二; P2 ZeRO
  * Stage 2): acc[i] = rep_0[i] + rep_1[i] + ... in ascending order, fp32 accumulator, each 16-bit
  * replica widened exactly. Optional outputs, any subset but at least one:
  *   out_grad      device float[n]: acc.
  *   d_nonfinite   device int32: set to 1 if any acc[i] is +-inf or NaN, otherwise left as is
  *                 (so several calls OR into it; the caller zeroes it first).
- *   d_sq_partials device double[ZERO_SQ_PARTIALS]: every entry overwritten; their sum is
- *                 sum_i (double(acc[i]) * sq_scale)^2 (finish with zero_shard_sqnorm).
- * n == 0 still zeroes d_sq_partials when given. Aliasing: out_grad must not overlap a replica.
- * Errors: bad source, no output, aliasing -> ZERO_E_INVAL; n*4 >= 2^64 -> ZERO_E_OVERFLOW. */
+ *   d_sq_partials device double[zero_sq_partials_len(n)]: entry t (t < ceil(n/512)) receives
+ *                 sum over i in [512t, 512t+512) of (double(acc[i]) * sq_scale)^2, each in a fixed
+ *                 order that does not depend on alignment; finish with zero_shard_sqnorm(NULL, n).
+ * n == 0 enqueues nothing. Aliasing: out_grad and d_sq_partials must not overlap a replica or each
+ * other. Errors: bad source, no output, aliasing -> ZERO_E_INVAL; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
 zero_status zero_reduce_shard(const zero_grad_src* src, uint64_t n, float* out_grad,
                               int32_t* d_nonfinite, double* d_sq_partials, double sq_scale,
                               void* stream);
 
-/* Squared L2 norm of a shard in fp64, for gradient clipping. With d_grad != NULL, first writes
- * the ZERO_SQ_PARTIALS partial sums of sum_i (double(d_grad[i]) * sq_scale)^2 into d_partials;
- * with d_grad == NULL, d_partials must already hold them (from zero_reduce_shard). Then writes
- * their sum, in a fixed order, to *d_out (device double). Errors: d_partials or d_out NULL ->
- * ZERO_E_INVAL. */
+/* Squared L2 norm of a shard in fp64, for gradient clipping. With d_grad != NULL, first writes the
+ * per-tile partials of sum_i (double(d_grad[i]) * sq_scale)^2 into d_partials (as
+ * zero_reduce_shard does); with d_grad == NULL, d_partials must already hold them from a
+ * zero_reduce_shard call over the same n. Then sums them in a fixed two-level order (contiguous
+ * chunks of ceil(tiles/1024) partials, then the chunk sums), using the buffer's last 1024 slots as
+ * scratch, and writes the result to *d_out (device double; 0 for n == 0). d_partials holds
+ * zero_sq_partials_len(n) doubles. Errors: d_partials or d_out NULL, d_out inside the partials or
+ * the gradient -> ZERO_E_INVAL; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
 zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, double* d_partials,
                               double* d_out, void* stream);
 

@@ -17,7 +17,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ze
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:zero_status|const char\*)\s+(zero_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:zero_status|const char\*|uint64_t)\s+(zero_\w+)\s*\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol():
@@ -41,7 +41,7 @@ def test_one_hip_runtime_in_process():
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define ZERO_MAX_REPLICAS (\d+)", text).group(1)) == Z.ZERO_MAX_REPLICAS
-    assert int(re.search(r"#define ZERO_SQ_PARTIALS (\d+)", text).group(1)) == Z.ZERO_SQ_PARTIALS
+    assert "ZERO_SQ_PARTIALS" not in text
     assert ctypes.sizeof(Z.ZeroPlan) == 40 and ctypes.sizeof(Z.ZeroAdamHParams) == 56
 
 
@@ -161,6 +161,13 @@ def test_device_entry_points_validate_first():
     assert L.zero_shard_sqnorm(None, 0, 1.0, None, fake, None) == 1
     assert L.zero_shard_sqnorm(None, 0, 1.0, fake, fake + 8, None) == 1
     assert "overlap" in Z.zero_last_error()
+
+
+def test_sq_partials_len():
+    # one partial per 512-element tile, then 1024 second-level slots
+    for n, want in ((0, 1024), (1, 1025), (512, 1025), (513, 1026), (813_491_520, 1_588_851 + 1024),
+                    (1 << 40, (1 << 31) + 1024)):
+        assert Z.zero_sq_partials_len(n) == want, n
 
 
 def test_status_strings():

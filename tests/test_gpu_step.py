@@ -3,6 +3,8 @@ finishes in seconds. Every comparison of fp32 state and 16-bit output is bit for
 and the oracle evaluate the same fp32 operation order with IEEE rounding); the squared norm, an
 fp64 sum in a different order, is held to 1e-10 relative."""
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -16,7 +18,7 @@ from workloads import host as H
 
 pytestmark = pytest.mark.gpu
 
-TILE = 2048  # elements per block tile of the kernels (256 threads x 4 x 2)
+TILE = 512  # elements per block tile of the Adam and reduce kernels (64 threads x 4 x 2)
 
 
 def _reps_np(rng, R, n, dtype, std=1e-3, valid=None):
@@ -209,7 +211,7 @@ def _reduce(reps_np, dtype, n, sq_scale=1.0, want_grad=True, offset=0):
     d_r = [dev_rep(np.concatenate([np.zeros(offset, reps_np.dtype), r]), dtype)[offset:] for r in reps_np]
     d_g = torch.full((n + offset,), 7.0, device=DEV)[offset:] if want_grad else None
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
-    parts = torch.full((Z.ZERO_SQ_PARTIALS,), 9.0, dtype=torch.float64, device=DEV)
+    parts = torch.full((Z.zero_sq_partials_len(n),), 9.0, dtype=torch.float64, device=DEV)
     out = torch.zeros(1, dtype=torch.float64, device=DEV)
     Z.zero_reduce_shard(d_r, n, d_g, flag, parts, sq_scale)
     Z.zero_shard_sqnorm(None, n, sq_scale, parts, out)
@@ -231,22 +233,45 @@ def test_reduce_matches_oracle(dtype, R):
     assert sq == pytest.approx(O.shard_sqnorm(acc, 2.0 ** -6), rel=1e-10, abs=0)
 
 
-@pytest.mark.parametrize("n", [1, 5, TILE - 1, TILE + 3, 5000 * TILE + 17])
+@pytest.mark.parametrize("n", [1, 5, TILE - 1, TILE + 3, 20000 * TILE + 17])
 def test_reduce_sizes_and_misalignment(n):
+    """Aligned arrays take the vector path for whole tiles, a replica one element off takes the
+    per-element path everywhere; the gradient, the per-tile partials and the norm must agree bit
+    for bit between the two (the element order inside a tile does not depend on the path)."""
     banner(f"reduce n={n}")
     rng = np.random.default_rng(n % 1000)
     reps = _reps_np(rng, 2, n, "bf16")
     acc = O.replica_sum(list(reps), "bf16")
+    seen = []
     for offset in (0, 1):
-        g, flag, sq, _ = _reduce(reps, "bf16", n, offset=offset)
+        g, flag, sq, parts = _reduce(reps, "bf16", n, offset=offset)
         assert_bits_equal(g, f32_bits(acc), f"reduced grad offset {offset}")
         assert sq == pytest.approx(O.shard_sqnorm(acc), rel=1e-10, abs=0)
+        seen.append((sq, parts[:-(1024)].copy()))
+    assert seen[0][0] == seen[1][0]
+    assert np.array_equal(seen[0][1], seen[1][1])
 
 
-def test_reduce_zero_size_zeroes_partials():
+def test_reduce_per_tile_partials():
+    """Partial t is the squared norm of tile t alone (elements [512t, 512t + 512))."""
+    n = 37 * TILE + 101
+    rng = np.random.default_rng(77)
+    reps = _reps_np(rng, 8, n, "f16")
+    acc = O.replica_sum(list(reps), "f16")
+    _, _, sq, parts = _reduce(reps, "f16", n, sq_scale=2.0 ** -6)
+    ntiles = -(-n // TILE)
+    assert Z.zero_sq_partials_len(n) == ntiles + 1024
+    for t in range(ntiles):
+        want = O.shard_sqnorm(acc[t * TILE:(t + 1) * TILE], 2.0 ** -6)
+        assert parts[t] == pytest.approx(want, rel=1e-12, abs=0), t
+    assert sq == pytest.approx(math.fsum(parts[:ntiles].tolist()), rel=1e-13, abs=0)
+
+
+def test_reduce_zero_size():
     reps = np.zeros((1, 4), np.float32)
     _, flag, sq, parts = _reduce(reps, "f32", 0)
-    assert sq == 0.0 and flag == 0 and not parts.any()
+    assert sq == 0.0 and flag == 0
+    assert (parts == 9.0).all()                  # n = 0 writes no partial
 
 
 @pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
@@ -266,7 +291,7 @@ def test_reduce_flags_nonfinite(bad):
 
 
 def test_reduce_is_deterministic():
-    n = 3000 * TILE + 3
+    n = 12000 * TILE + 3
     rng = np.random.default_rng(6)
     reps = _reps_np(rng, 4, n, "f16")
     a = _reduce(reps, "f16", n, sq_scale=2.0 ** -16)
@@ -278,7 +303,7 @@ def test_sqnorm_from_fp32_grad():
     for n in (1, 1000, 77 * TILE + 5):
         rng = np.random.default_rng(n)
         g = (rng.standard_normal(n) * 3).astype(np.float32)
-        parts = torch.zeros(Z.ZERO_SQ_PARTIALS, dtype=torch.float64, device=DEV)
+        parts = torch.zeros(Z.zero_sq_partials_len(n), dtype=torch.float64, device=DEV)
         out = torch.zeros(1, dtype=torch.float64, device=DEV)
         Z.zero_shard_sqnorm(dev_f32(g), n, 0.5, parts, out)
         torch.cuda.synchronize()
@@ -292,7 +317,7 @@ def _two_pass(reps_np, n, master, loss_scale, max_norm, hp_kw):
     d_r = [dev_rep(r, "f16") for r in reps_np]
     d_g = torch.empty(n, device=DEV)
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
-    parts = torch.empty(Z.ZERO_SQ_PARTIALS, dtype=torch.float64, device=DEV)
+    parts = torch.empty(Z.zero_sq_partials_len(n), dtype=torch.float64, device=DEV)
     sq = torch.empty(1, dtype=torch.float64, device=DEV)
     Z.zero_reduce_shard(d_r, n, d_g, flag, parts, 1.0 / loss_scale)
     Z.zero_shard_sqnorm(None, n, 1.0 / loss_scale, parts, sq)

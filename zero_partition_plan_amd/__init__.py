@@ -17,15 +17,14 @@ import torch  # noqa: F401  (loaded first so the library binds to the HIP runtim
 
 __all__ = [
     "ZeroError", "ZeroPlan", "ZeroAdamHParams", "ZeroAdamScalars", "lib", "lib_path",
-    "ZERO_MAX_REPLICAS", "ZERO_SQ_PARTIALS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
+    "ZERO_MAX_REPLICAS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
     "ZERO_ADAMW", "ZERO_ADAM_L2", "adam_hparams",
     "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_adam_derive",
-    "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
+    "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
     "zero_status_str", "zero_last_error",
 ]
 
 ZERO_MAX_REPLICAS = 64
-ZERO_SQ_PARTIALS = 2048
 ZERO_OK, ZERO_E_INVAL, ZERO_E_OVERFLOW, ZERO_E_UNSUPPORTED, ZERO_E_HIP = range(5)
 ZERO_F32, ZERO_F16, ZERO_BF16 = 0, 1, 2
 ZERO_ADAMW, ZERO_ADAM_L2 = 0, 1
@@ -102,6 +101,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        L.zero_sq_partials_len.argtypes = [u64]
+        L.zero_sq_partials_len.restype = u64
         L.zero_status_str.argtypes = [ctypes.c_int]
         L.zero_status_str.restype = ctypes.c_char_p
         L.zero_last_error.argtypes = []
@@ -186,20 +187,25 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def zero_sq_partials_len(n: int) -> int:
+    """Doubles the squared-norm partials buffer needs for a shard of n elements."""
+    return int(lib().zero_sq_partials_len(n))
+
+
 def zero_reduce_shard(reps, n: int, out_grad=None, nonfinite=None, sq_partials=None,
                       sq_scale: float = 1.0, stream=None):
     src, keep = _src(reps, n)
     _check(lib().zero_reduce_shard(
         ctypes.byref(src), n, _ptr(out_grad, n, "out_grad", (torch.float32,)),
         _ptr(nonfinite, 1, "nonfinite", (torch.int32,)),
-        _ptr(sq_partials, ZERO_SQ_PARTIALS, "sq_partials", (torch.float64,)),
+        _ptr(sq_partials, zero_sq_partials_len(n), "sq_partials", (torch.float64,)),
         float(sq_scale), _stream(stream)), "zero_reduce_shard")
 
 
 def zero_shard_sqnorm(grad, n: int, sq_scale: float, partials, out, stream=None):
     _check(lib().zero_shard_sqnorm(
         _ptr(grad, n, "grad", (torch.float32,)), n, float(sq_scale),
-        _ptr(partials, ZERO_SQ_PARTIALS, "partials", (torch.float64,)),
+        _ptr(partials, zero_sq_partials_len(n), "partials", (torch.float64,)),
         _ptr(out, 1, "out", (torch.float64,)), _stream(stream)), "zero_shard_sqnorm")
 
 

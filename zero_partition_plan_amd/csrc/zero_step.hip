@@ -20,9 +20,6 @@
 #ifndef ZERO_ADAM_SUB
 #define ZERO_ADAM_SUB 2            // 4-element groups per thread per tile in the Adam kernel
 #endif
-#ifndef ZERO_REDUCE_SUB
-#define ZERO_REDUCE_SUB 2          // same for the reduce / squared-norm kernel
-#endif
 #ifndef ZERO_NT
 #define ZERO_NT 1                  // streaming (non-temporal) loads and stores: data is touched once
 #endif
@@ -257,13 +254,26 @@ __global__ __launch_bounds__(kBlock) void k_adam_tail(RepPtrs reps, int nrep, ui
 // ---------------------------------------------------------------------------------------------
 // reduce pass: replica sum -> fp32 gradient, non-finite flag, fp64 squared-norm partials
 //
-// The grid is a function of n alone (min(ZERO_SQ_PARTIALS, tiles)), each thread adds its own
-// elements in a fixed order, and the block sum uses a fixed butterfly, so the partials are
-// bit-reproducible. No atomics: the flag is only ever set to 1 by plain stores.
+// One single-wave block per tile of kRedTile elements. Thread `lane` owns the elements
+// base + u*256 + lane*4 + q (u < 2, q < 4) and adds their fp64 squares in that (u, q) order; the
+// 64 lane sums are combined by a fixed xor butterfly and lane 0 writes partial[tile]. The vector
+// path (whole, aligned tiles) and the per-element path (ragged last tile, unaligned arrays) use
+// the same element-to-lane map and order, so a partial never depends on alignment. The finish is
+// a fixed two-level sum (zero_shard_sqnorm), so the squared norm is bit-reproducible for a given
+// input and n. No atomics: the flag is only ever set to 1 by plain stores.
 
-__device__ __forceinline__ double block_sum(double x, double* lds) {
+constexpr int kRedSub = 2;
+constexpr uint64_t kRedTile = 64 * 4 * kRedSub;   // 512 elements
+constexpr uint32_t kSqLevel1 = 1024;               // second-level partial slots
+
+__device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;  // lane 0's value is the fixed-order result
+}
+
+__device__ __forceinline__ double block_sum(double x, double* lds) {
+  x = wave_sum(x);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) lds[wave] = x;
   __syncthreads();
@@ -280,69 +290,69 @@ __device__ __forceinline__ bool nonfinite(float x) {
   return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u;
 }
 
-template <int RDT, bool VEC, int RFIX>
-__global__ __launch_bounds__(kBlock) void k_reduce(RepPtrs reps, int nrep, uint64_t n,
-                                                   float* __restrict__ G, int32_t* __restrict__ flag,
-                                                   double* __restrict__ partials, double sq_scale) {
-  constexpr int SUB = ZERO_REDUCE_SUB;
-  constexpr uint64_t kTile = (uint64_t)kBlock * 4 * SUB;
-  __shared__ double lds[kWaves];
-  const uint64_t ntiles = (n + kTile - 1) / kTile;
+template <int RDT, int RFIX, bool VEC>
+__global__ __launch_bounds__(64) void k_reduce(RepPtrs reps, int nrep, uint64_t first_tile,
+                                               uint64_t n, float* __restrict__ G,
+                                               int32_t* __restrict__ flag,
+                                               double* __restrict__ partials, double sq_scale) {
+  const uint64_t tile = first_tile + blockIdx.x;
+  const uint64_t base = tile * kRedTile;
   double sq = 0.0;
   bool bad = false;
-  for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const uint64_t base = t * kTile;
-    if (VEC && base + kTile <= n) {
-      uint64_t idx[SUB];
+  if constexpr (VEC) {
+    uint64_t idx[kRedSub];
 #pragma unroll
-      for (int u = 0; u < SUB; ++u) idx[u] = base + (uint64_t)u * (kBlock * 4) + threadIdx.x * 4u;
-      f32x4 acc[SUB];
-      sum_reps4<RDT, RFIX, SUB>(reps, nrep, idx, acc);
+    for (int u = 0; u < kRedSub; ++u) idx[u] = base + (uint64_t)u * 256 + threadIdx.x * 4u;
+    f32x4 acc[kRedSub];
+    sum_reps4<RDT, RFIX, kRedSub>(reps, nrep, idx, acc);
 #pragma unroll
-      for (int u = 0; u < SUB; ++u) {
-        if (G != nullptr) st(reinterpret_cast<f32x4*>(G + idx[u]), acc[u]);
+    for (int u = 0; u < kRedSub; ++u) {
+      if (G != nullptr) st(reinterpret_cast<f32x4*>(G + idx[u]), acc[u]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bad |= nonfinite(acc[u][q]);
-          const double d = (double)acc[u][q] * sq_scale;
-          sq += d * d;
-        }
+      for (int q = 0; q < 4; ++q) {
+        bad |= nonfinite(acc[u][q]);
+        const double d = (double)acc[u][q] * sq_scale;
+        sq += d * d;
       }
-    } else {
-      const int R = RFIX ? RFIX : nrep;
-      for (int j = 0; j < (int)(kTile / kBlock); ++j) {
-        const uint64_t i = base + (uint64_t)j * kBlock + threadIdx.x;
+    }
+  } else {
+    for (int u = 0; u < kRedSub; ++u)
+      for (int q = 0; q < 4; ++q) {
+        const uint64_t i = base + (uint64_t)u * 256 + threadIdx.x * 4u + q;
         if (i < n) {
-          const float a = sum_reps1<RDT>(reps, R, i);
+          const float a = sum_reps1<RDT>(reps, nrep, i);
           if (G != nullptr) G[i] = a;
           bad |= nonfinite(a);
           const double d = (double)a * sq_scale;
           sq += d * d;
         }
       }
-    }
   }
-  if (flag != nullptr) {
-    if (__syncthreads_or(bad) && threadIdx.x == 0) *flag = 1;
-  }
+  if (flag != nullptr && __ballot(bad) != 0 && threadIdx.x == 0) *flag = 1;
   if (partials != nullptr) {
-    const double s = block_sum(sq, lds);
-    if (threadIdx.x == 0) partials[blockIdx.x] = s;
-    if (blockIdx.x == 0)
-      for (uint32_t i = gridDim.x + threadIdx.x; i < ZERO_SQ_PARTIALS; i += kBlock) partials[i] = 0.0;
+    sq = wave_sum(sq);
+    if (threadIdx.x == 0) partials[tile] = sq;
   }
 }
 
-__global__ __launch_bounds__(kBlock) void k_zero_partials(double* __restrict__ partials) {
-  for (uint32_t i = threadIdx.x; i < ZERO_SQ_PARTIALS; i += kBlock) partials[i] = 0.0;
+// level 1: block b sums partials [b*chunk, min(ntiles, (b+1)*chunk)) into partials[ntiles + b]
+__global__ __launch_bounds__(kBlock) void k_sq_level1(double* __restrict__ partials, uint64_t ntiles,
+                                                      uint64_t chunk) {
+  __shared__ double lds[kWaves];
+  const uint64_t lo = (uint64_t)blockIdx.x * chunk;
+  const uint64_t hi = lo + chunk < ntiles ? lo + chunk : ntiles;
+  double s = 0.0;
+  for (uint64_t i = lo + threadIdx.x; i < hi; i += kBlock) s += partials[i];
+  s = block_sum(s, lds);
+  if (threadIdx.x == 0) partials[ntiles + blockIdx.x] = s;
 }
 
-__global__ __launch_bounds__(kBlock) void k_sq_finalize(const double* __restrict__ partials,
-                                                        double* __restrict__ out) {
+// level 2: one block sums the `count` level-1 values at `l1` into *out
+__global__ __launch_bounds__(kBlock) void k_sq_finalize(const double* __restrict__ l1,
+                                                        uint32_t count, double* __restrict__ out) {
   __shared__ double lds[kWaves];
   double s = 0.0;
-#pragma unroll
-  for (int j = 0; j < ZERO_SQ_PARTIALS / kBlock; ++j) s += partials[threadIdx.x + j * kBlock];
+  for (uint32_t i = threadIdx.x; i < count; i += kBlock) s += l1[i];
   s = block_sum(s, lds);
   if (threadIdx.x == 0) *out = s;
 }
@@ -406,7 +416,6 @@ RepPtrs rep_ptrs(const zero_grad_src* src) {
 
 // ----- Adam dispatch
 
-constexpr uint64_t kReduceTile = (uint64_t)kBlock * 4 * ZERO_REDUCE_SUB;
 constexpr uint64_t kAdamTile = (uint64_t)kAdamBlock * 4 * ZERO_ADAM_SUB;
 constexpr uint64_t kMaxGrid = 1u << 24;  // blocks per Adam launch; keeps grid * block below 2^32
 
@@ -471,6 +480,8 @@ void adam_by_out(const AdamArgs& a, int odt, bool l2) {
 
 // ----- reduce dispatch
 
+uint64_t red_tiles(uint64_t n) { return (n + kRedTile - 1) / kRedTile; }
+
 struct ReduceArgs {
   RepPtrs reps;
   int nrep;
@@ -479,57 +490,63 @@ struct ReduceArgs {
   int32_t* flag;
   double* partials;
   double sq_scale;
-  dim3 grid;
   hipStream_t stream;
 };
 
-template <int RDT, bool VEC, int RFIX>
-void launch_reduce(const ReduceArgs& a) {
-  hipLaunchKernelGGL((k_reduce<RDT, VEC, RFIX>), a.grid, dim3(kBlock), 0, a.stream, a.reps, a.nrep,
-                     a.n, a.G, a.flag, a.partials, a.sq_scale);
-}
-
-template <int RDT>
-void reduce_by_r(const ReduceArgs& a, bool vec) {
-  if (!vec) return launch_reduce<RDT, false, 0>(a);
-  switch (a.nrep) {
-    case 1: launch_reduce<RDT, true, 1>(a); break;
-    case 8: launch_reduce<RDT, true, 8>(a); break;
-    case 16: launch_reduce<RDT, true, 16>(a); break;
-    case 64: launch_reduce<RDT, true, 64>(a); break;
-    default: launch_reduce<RDT, true, 0>(a); break;
+// tiles [t0, t1) in grids of at most kMaxGrid blocks
+template <int RDT, int RFIX, bool VEC>
+void launch_reduce(const ReduceArgs& a, uint64_t t0, uint64_t t1) {
+  for (uint64_t t = t0; t < t1; t += kMaxGrid) {
+    const uint64_t g = t1 - t < kMaxGrid ? t1 - t : kMaxGrid;
+    hipLaunchKernelGGL((k_reduce<RDT, RFIX, VEC>), dim3((unsigned)g), dim3(64), 0, a.stream, a.reps,
+                       a.nrep, t, a.n, a.G, a.flag, a.partials, a.sq_scale);
   }
 }
 
-
-dim3 reduce_grid(uint64_t n) {
-  const uint64_t tiles = (n + kReduceTile - 1) / kReduceTile;
-  return dim3((unsigned)(tiles < ZERO_SQ_PARTIALS ? (tiles ? tiles : 1) : ZERO_SQ_PARTIALS));
+template <int RDT>
+void reduce_kernels(const ReduceArgs& a, bool vec) {
+  const uint64_t all = red_tiles(a.n), full = vec ? a.n / kRedTile : 0;
+  switch (a.nrep) {
+    case 1: launch_reduce<RDT, 1, true>(a, 0, full); break;
+    case 8: launch_reduce<RDT, 8, true>(a, 0, full); break;
+    case 16: launch_reduce<RDT, 16, true>(a, 0, full); break;
+    case 64: launch_reduce<RDT, 64, true>(a, 0, full); break;
+    default: launch_reduce<RDT, 0, true>(a, 0, full); break;
+  }
+  launch_reduce<RDT, 0, false>(a, full, all);  // ragged last tile, or every tile if unaligned
 }
 
 zero_status reduce_impl(const zero_grad_src* src, uint64_t n, float* G, int32_t* flag,
                         double* partials, double sq_scale, hipStream_t stream, const char* what) {
-  if (n == 0) {
-    if (partials != nullptr) {
-      hipLaunchKernelGGL(k_zero_partials, dim3(1), dim3(kBlock), 0, stream, partials);
-      return launched(what);
-    }
-    return zero::ok();
-  }
-  ReduceArgs a{rep_ptrs(src), (int)src->count, n, G, flag, partials, sq_scale, reduce_grid(n), stream};
+  if (n == 0) return zero::ok();
+  ReduceArgs a{rep_ptrs(src), (int)src->count, n, G, flag, partials, sq_scale, stream};
   const bool vec = src_aligned(src) && (G == nullptr || aligned(G, 16));
   (void)hipGetLastError();
   switch (src->dtype) {
-    case ZERO_F32: reduce_by_r<ZERO_F32>(a, vec); break;
-    case ZERO_F16: reduce_by_r<ZERO_F16>(a, vec); break;
-    default: reduce_by_r<ZERO_BF16>(a, vec); break;
+    case ZERO_F32: reduce_kernels<ZERO_F32>(a, vec); break;
+    case ZERO_F16: reduce_kernels<ZERO_F16>(a, vec); break;
+    default: reduce_kernels<ZERO_BF16>(a, vec); break;
   }
+  return launched(what);
+}
+
+zero_status sq_finish(uint64_t n, double* partials, double* out, hipStream_t stream, const char* what) {
+  const uint64_t ntiles = red_tiles(n);
+  const uint32_t g1 = ntiles < kSqLevel1 ? (uint32_t)ntiles : kSqLevel1;
+  (void)hipGetLastError();
+  if (g1 > 0) {
+    const uint64_t chunk = (ntiles + g1 - 1) / g1;
+    hipLaunchKernelGGL(k_sq_level1, dim3(g1), dim3(kBlock), 0, stream, partials, ntiles, chunk);
+  }
+  hipLaunchKernelGGL(k_sq_finalize, dim3(1), dim3(kBlock), 0, stream, partials + ntiles, g1, out);
   return launched(what);
 }
 
 }  // namespace
 
 extern "C" {
+
+uint64_t zero_sq_partials_len(uint64_t n) { return red_tiles(n) + kSqLevel1; }
 
 zero_status zero_reduce_shard(const zero_grad_src* src, uint64_t n, float* out_grad,
                               int32_t* d_nonfinite, double* d_sq_partials, double sq_scale,
@@ -539,14 +556,14 @@ zero_status zero_reduce_shard(const zero_grad_src* src, uint64_t n, float* out_g
   if (s != ZERO_OK) return s;
   if (!out_grad && !d_nonfinite && !d_sq_partials)
     return zero::fail(ZERO_E_INVAL, "%s: no output requested", fn);
-  const uint64_t rb = n * zero::dtype_bytes(src->dtype);
-  if (out_grad) {
-    for (uint32_t k = 0; k < src->count; ++k)
-      if (zero::overlaps(out_grad, n * 4, src->ptrs[k], rb))
-        return zero::fail(ZERO_E_INVAL, "%s: out_grad overlaps replica %u", fn, k);
+  const uint64_t rb = n * zero::dtype_bytes(src->dtype), pb = zero_sq_partials_len(n) * 8;
+  for (uint32_t k = 0; k < src->count; ++k) {
+    if (out_grad && zero::overlaps(out_grad, n * 4, src->ptrs[k], rb))
+      return zero::fail(ZERO_E_INVAL, "%s: out_grad overlaps replica %u", fn, k);
+    if (d_sq_partials && zero::overlaps(d_sq_partials, pb, src->ptrs[k], rb))
+      return zero::fail(ZERO_E_INVAL, "%s: partials overlap replica %u", fn, k);
   }
-  if (d_sq_partials && out_grad &&
-      zero::overlaps(d_sq_partials, ZERO_SQ_PARTIALS * 8, out_grad, n * 4))
+  if (d_sq_partials && out_grad && zero::overlaps(d_sq_partials, pb, out_grad, n * 4))
     return zero::fail(ZERO_E_INVAL, "%s: partials overlap out_grad", fn);
   return reduce_impl(src, n, out_grad, d_nonfinite, d_sq_partials, sq_scale,
                      static_cast<hipStream_t>(stream), fn);
@@ -556,7 +573,10 @@ zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, 
                               double* d_out, void* stream) {
   const char* fn = "zero_shard_sqnorm";
   if (!d_partials || !d_out) return zero::fail(ZERO_E_INVAL, "%s: partials or out is NULL", fn);
-  if (zero::overlaps(d_partials, ZERO_SQ_PARTIALS * 8, d_out, 8))
+  if (n > UINT64_MAX / 8)
+    return zero::fail(ZERO_E_OVERFLOW, "%s: n = %llu too large", fn, (unsigned long long)n);
+  const uint64_t pb = zero_sq_partials_len(n) * 8;
+  if (zero::overlaps(d_partials, pb, d_out, 8))
     return zero::fail(ZERO_E_INVAL, "%s: out overlaps the partials", fn);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (d_grad != nullptr) {
@@ -564,14 +584,14 @@ zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, 
     const zero_grad_src src{ptrs, 1, ZERO_F32};
     zero_status s = check_src(fn, &src, n);
     if (s != ZERO_OK) return s;
-    if (zero::overlaps(d_partials, ZERO_SQ_PARTIALS * 8, d_grad, n * 4))
+    if (zero::overlaps(d_partials, pb, d_grad, n * 4))
       return zero::fail(ZERO_E_INVAL, "%s: partials overlap the gradient", fn);
+    if (zero::overlaps(d_out, 8, d_grad, n * 4))
+      return zero::fail(ZERO_E_INVAL, "%s: out overlaps the gradient", fn);
     s = reduce_impl(&src, n, nullptr, nullptr, d_partials, sq_scale, st, fn);
     if (s != ZERO_OK) return s;
   }
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(k_sq_finalize, dim3(1), dim3(kBlock), 0, st, d_partials, d_out);
-  return launched(fn);
+  return sq_finish(n, d_partials, d_out, st, fn);
 }
 
 zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float grad_scale,

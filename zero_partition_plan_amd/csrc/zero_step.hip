@@ -43,6 +43,7 @@ constexpr int kAdamBlock = ZERO_ADAM_BLOCK;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct RepPtrs {
   const void* p[ZERO_MAX_REPLICAS];
@@ -80,16 +81,24 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// fp32 -> bf16, round to nearest even; NaN keeps sign and top payload and is made quiet.
-__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
-  const uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// fp32 -> 16-bit, round to nearest even, two values packed low-then-high. bf16 uses gfx950's
+// v_cvt_pk_bf16_f32: checked against the integer rule (u + 0x7fff + ((u >> 16) & 1)) >> 16, with a
+// NaN becoming (u >> 16) | 0x40, on all 2^32 fp32 patterns in this build's floating-point mode.
+// binary16 uses the IEEE conversion in the default rounding mode.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <int ODT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2 x = {a, b};
+  if constexpr (ODT == ZERO_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
 }
 
-// fp32 -> IEEE binary16, round to nearest even (the hardware conversion in the default mode).
-__device__ __forceinline__ uint32_t f32_to_f16(float x) {
-  return __builtin_bit_cast(uint16_t, (_Float16)x);
+template <int ODT>
+__device__ __forceinline__ uint16_t to_out1(float x) {
+  if constexpr (ODT == ZERO_BF16) return __builtin_bit_cast(uint16_t, (__bf16)x);
+  else return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
 // 4 consecutive replica elements starting at element i (vector path: i is a multiple of 4 and
@@ -121,12 +130,6 @@ __device__ __forceinline__ float ld_rep1(const void* base, uint64_t i) {
   if constexpr (RDT == ZERO_F32) return static_cast<const float*>(base)[i];
   else if constexpr (RDT == ZERO_BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
   else return f16_to_f32(static_cast<const uint16_t*>(base)[i]);
-}
-
-template <int ODT>
-__device__ __forceinline__ uint32_t to_out(float x) {
-  if constexpr (ODT == ZERO_BF16) return f32_to_bf16(x);
-  else return f32_to_f16(x);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -224,8 +227,8 @@ __global__ __launch_bounds__(kAdamBlock) ZERO_ADAM_WAVES_ATTR void k_adam_step(
     st(reinterpret_cast<f32x4*>(V + idx[u]), v[u]);
     if constexpr (ODT != ZERO_F32) {
       u32x2 o;
-      o.x = to_out<ODT>(p[u].x) | (to_out<ODT>(p[u].y) << 16);
-      o.y = to_out<ODT>(p[u].z) | (to_out<ODT>(p[u].w) << 16);
+      o.x = pack2<ODT>(p[u].x, p[u].y);
+      o.y = pack2<ODT>(p[u].z, p[u].w);
       st(reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx[u]), o);
     }
   }
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kBlock) void k_adam_tail(RepPtrs reps, int nrep, ui
     P[i] = p;
     M[i] = m;
     V[i] = v;
-    if constexpr (ODT != ZERO_F32) static_cast<uint16_t*>(out)[i] = (uint16_t)to_out<ODT>(p);
+    if constexpr (ODT != ZERO_F32) static_cast<uint16_t*>(out)[i] = to_out1<ODT>(p);
   }
 }
 

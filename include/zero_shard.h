@@ -21,7 +21,7 @@
  *     never synchronised; device outputs are valid once the stream reaches that point.
  *   - Errors: arguments are checked before any device work; on a bad argument nothing is launched
  *     and nothing is written. A failed launch returns ZERO_E_HIP. Details: zero_last_error().
- *   - n == 0 is valid and enqueues nothing (except where stated).
+ *   - n == 0 is valid and enqueues nothing (except where stated); arrays of length 0 may be NULL.
  *   - Results are deterministic: a given input and size always produces the same bits.
  */
 #ifndef ZERO_SHARD_H

@@ -170,6 +170,22 @@ def test_sq_partials_len():
         assert Z.zero_sq_partials_len(n) == want, n
 
 
+def test_zero_length_calls_accept_null_arrays():
+    """n = 0 is a no-op that still validates counts, dtypes and hyper-parameters, and returns
+    before any HIP call, so it runs on the CPU."""
+    L = Z.lib()
+    hp = Z.adam_hparams()
+    src, keep = _src([0, 0], Z.ZERO_BF16)
+    assert L.zero_adam_shard_step(ctypes.byref(src), 0, 1.0, None, None, None, ctypes.byref(hp),
+                                  None, 0, None, None) == 0
+    assert L.zero_reduce_shard(ctypes.byref(src), 0, None, None, 1 << 40, 1.0, None) == 0
+    bad_hp = Z.adam_hparams(step=0)
+    assert L.zero_adam_shard_step(ctypes.byref(src), 0, 1.0, None, None, None, ctypes.byref(bad_hp),
+                                  None, 0, None, None) == 1
+    too_many, keep2 = _src([0] * 65)
+    assert L.zero_reduce_shard(ctypes.byref(too_many), 0, None, None, 1 << 40, 1.0, None) == 1
+
+
 def test_status_strings():
     for s in range(5):
         assert Z.zero_status_str(s)

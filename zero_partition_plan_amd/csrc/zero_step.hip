@@ -395,7 +395,7 @@ zero_status check_src(const char* fn, const zero_grad_src* src, uint64_t n) {
                       ZERO_MAX_REPLICAS);
   if (!zero::dtype_valid(src->dtype))
     return zero::fail(ZERO_E_INVAL, "%s: unknown replica dtype %d", fn, src->dtype);
-  for (uint32_t k = 0; k < src->count; ++k)
+  for (uint32_t k = 0; k < src->count && n > 0; ++k)   // zero-length arrays may be NULL
     if (!src->ptrs[k]) return zero::fail(ZERO_E_INVAL, "%s: replica %u is NULL", fn, k);
   if (n > UINT64_MAX / 8) return zero::fail(ZERO_E_OVERFLOW, "%s: n = %llu too large", fn,
                                             (unsigned long long)n);
@@ -604,7 +604,8 @@ zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float gra
   const char* fn = "zero_adam_shard_step";
   zero_status s = check_src(fn, src, n);
   if (s != ZERO_OK) return s;
-  if (!master || !m || !v) return zero::fail(ZERO_E_INVAL, "%s: master, m or v is NULL", fn);
+  if (n > 0 && (!master || !m || !v))
+    return zero::fail(ZERO_E_INVAL, "%s: master, m or v is NULL", fn);
   zero_adam_scalars k;
   s = zero_adam_derive(hp, &k);
   if (s != ZERO_OK) return s;

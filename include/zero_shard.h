@@ -107,6 +107,22 @@ zero_status zero_shard_range(const zero_plan* p, uint32_t rank, uint64_t* begin,
 zero_status zero_stage_bytes(const zero_plan* p, uint32_t stage, uint32_t param_b, uint32_t grad_b,
                              uint32_t opt_b, uint64_t out[4]);
 
+/* The stage-choice rule of P1 section 四 (its decision tree: a card that can hold the whole model
+ * takes ZeRO-1, one that can still hold parameters and gradients takes ZeRO-2, otherwise ZeRO-3 with
+ * optimizer-state offload advised), read as: the smallest stage of 1..3 whose per-rank bytes
+ * (zero_stage_bytes of this plan) are <= usable_bytes, the caller's budget after whatever it keeps
+ * for activations and buffers; if none fits, stage 3 with offload_advised = 1. bytes[] is the chosen
+ * stage's optimizer, gradient, parameter and total bytes. Host only. Errors: NULL, an inconsistent
+ * plan -> ZERO_E_INVAL; a byte count >= 2^64 -> ZERO_E_OVERFLOW. */
+typedef struct {
+  uint32_t stage;           /* 1, 2 or 3 */
+  uint32_t offload_advised; /* 1 when even ZeRO-3 does not fit the budget */
+  uint64_t bytes[4];
+} zero_stage_choice;
+
+zero_status zero_choose_stage(const zero_plan* p, uint64_t usable_bytes, uint32_t param_b,
+                              uint32_t grad_b, uint32_t opt_b, zero_stage_choice* out);
+
 /* The fp32 constants of step hp->step, each formed in fp64 and rounded once:
  * b1 = f32(beta1), b2 = f32(beta2), c1 = f32(1-beta1), c2 = f32(1-beta2),
  * ss = f32(lr / (1 - pow(beta1, t))), bc = f32(sqrt(1 - pow(beta2, t))), e = f32(eps),

@@ -22,7 +22,8 @@ Modules:
   adam       replica sum, non-finite flag, squared norm, clip coefficient,
              Adam/AdamW update and the full per-rank step                          [P1 二; P2 Stage 1/2]
   cast       fp32 -> bf16 / fp16 round-to-nearest-even (bit patterns as uint16)  [P1 一; P3 comparisons]
-  memory     per-stage model-state bytes per rank (DP, ZeRO-1/2/3)               [P1 一/二; P3 stages]
+  memory     per-stage model-state bytes per rank (DP, ZeRO-1/2/3) and the
+             stage-choice rule                                                  [P1 一/二/四; P3 stages]
 
 Parity status of each function is stated in its docstring; the clip-coefficient formula is
 "parity unpinned" (no page defines it).
@@ -42,12 +43,12 @@ from .adam import (
     sharded_step,
     unsharded_step,
 )
-from .memory import MemoryEstimation, estimate_memory_per_gpu, stage_bytes_exact, STAGES
+from .memory import MemoryEstimation, estimate_memory_per_gpu, stage_bytes_exact, STAGES, choose_stage
 
 __all__ = [
     "Plan", "partition_plan", "shard_range",
     "cast_bf16_rne", "cast_fp16_rne", "widen_bf16", "widen_fp16",
     "AdamHParams", "AdamScalars", "adam_scalars", "adam_update", "replica_sum",
     "nonfinite_flag", "shard_sqnorm", "clip_coefficient", "sharded_step", "unsharded_step",
-    "MemoryEstimation", "estimate_memory_per_gpu", "stage_bytes_exact", "STAGES",
+    "MemoryEstimation", "estimate_memory_per_gpu", "stage_bytes_exact", "STAGES", "choose_stage",
 ]

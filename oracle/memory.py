@@ -9,6 +9,15 @@ that rule in its own form: a table of which component each stage shards.
 
 ``stage_bytes_exact`` is the integer variant for a concrete plan: a sharded component costs
 S (the padded shard size) elements per rank instead of N/Nd.
+
+``choose_stage`` is the stage-choice rule of [P1] section 四 (a decision tree: a card that can hold
+the whole model takes ZeRO-1; one that cannot, but can hold parameters and gradients, takes ZeRO-2;
+one that cannot even hold the parameters needs ZeRO-3, with optimizer-state offload advised). The
+page does not say against which budget "hold" is judged; the reading here is: the smallest stage of
+1..3 whose exact per-rank model-state bytes fit in the caller's usable byte budget (card capacity
+less what the caller reserves for activations and buffers), and ZeRO-3 plus the offload advice when
+none fits. Pinned to the page's three examples (7B, 13B, 70B on an 80 GB card) under a stated
+reading of their unstated data-parallel degree and reserve.
 """
 
 from __future__ import annotations
@@ -60,3 +69,15 @@ def stage_bytes_exact(plan: Plan, stage: int, param_b: int = 2, grad_b: int = 2,
     if total >= 1 << 64:
         raise OverflowError("byte count does not fit in 64 bits")
     return comp[0], comp[1], comp[2], total
+
+
+def choose_stage(plan: Plan, usable_bytes: int, param_b: int = 2, grad_b: int = 2,
+                 opt_b: int = 12) -> tuple[int, bool, tuple[int, int, int, int]]:
+    """(stage 1..3, offload advised, that stage's per-rank bytes) for a budget of usable bytes."""
+    if usable_bytes < 0:
+        raise ValueError("usable_bytes must be >= 0")
+    for stage in (1, 2, 3):
+        b = stage_bytes_exact(plan, stage, param_b, grad_b, opt_b)
+        if b[3] <= usable_bytes:
+            return stage, False, b
+    return 3, True, stage_bytes_exact(plan, 3, param_b, grad_b, opt_b)

@@ -93,6 +93,18 @@ def test_stage_bytes_match_oracle():
     assert e.value.status == 2
 
 
+def test_choose_stage_matches_oracle():
+    for n in (0, 1, 999, 7_000_000_000, 13_000_000_000, 70_000_000_000, 174_604_259_328):
+        for nd in (1, 3, 8, 64):
+            for usable in (0, 10**9, 60 * 10**9, 80 * 10**9, 288 * 10**9, (1 << 64) - 1):
+                plan_c, plan_o = Z.zero_partition_plan(n, nd), O.partition_plan(n, nd)
+                for pb, gb, ob in ((2, 2, 12), (2, 4, 12), (4, 4, 8)):
+                    assert Z.zero_choose_stage(plan_c, usable, pb, gb, ob) == \
+                        O.choose_stage(plan_o, usable, pb, gb, ob), (n, nd, usable, pb, gb, ob)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_choose_stage(Z.zero_partition_plan(1 << 62, 1), 0, 8, 8, 8)   # byte overflow
+
+
 def test_adam_scalars_match_oracle_bitwise():
     rng = np.random.default_rng(9)
     cases = [dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=t) for t in (1, 2, 11, 1000)]

@@ -94,3 +94,46 @@ def test_exact_bytes_with_padding_use_shard_size():
     assert O.stage_bytes_exact(p, 3) == (12 * 250_001, 2 * 250_001, 2 * 250_001, 16 * 250_001)
     assert O.stage_bytes_exact(p, 1, 2, 4, 12) == (12 * 250_001, 4 * 1_000_003, 2 * 1_000_003,
                                                    12 * 250_001 + 6 * 1_000_003)
+
+
+def test_stage_choice_page_examples():
+    f = FIG["stage_choice_examples"]
+    usable = int(f["card_bytes"] * 0.75)
+    for c in f["cases"]:
+        plan = O.partition_plan(int(c["num_params"]), 8)
+        stage, offload, b = O.choose_stage(plan, usable)
+        assert (stage, offload) == (c["stage"], c["offload"]), c
+        assert b == O.stage_bytes_exact(plan, stage)
+
+
+def test_stage_choice_reserve_window_of_the_reading():
+    """The reading's claim: at Nd = 8 every budget between the 13B ZeRO-2 footprint and the 13B
+    ZeRO-1 footprint reproduces the page's three answers, and budgets outside it do not."""
+    plans = {n: O.partition_plan(int(n), 8) for n in (7e9, 13e9, 70e9)}
+    lo = O.stage_bytes_exact(plans[13e9], 2)[3]
+    hi = O.stage_bytes_exact(plans[13e9], 1)[3]
+    assert 0.10 < 1 - hi / 80e9 < 0.12 and 0.38 < 1 - lo / 80e9 < 0.40
+    for usable in (lo, (lo + hi) // 2, hi - 1):
+        got = [O.choose_stage(plans[n], usable)[:2] for n in (7e9, 13e9, 70e9)]
+        assert got == [(1, False), (2, False), (3, True)]
+    assert O.choose_stage(plans[13e9], hi)[0] == 1
+    assert O.choose_stage(plans[13e9], lo - 1)[0] == 3
+
+
+def test_stage_choice_is_monotone():
+    """More parameters never pick a lower stage; a bigger budget never picks a higher one; more
+    ranks never pick a higher one."""
+    budgets = [int(x * 1e9) for x in (8, 16, 40, 60, 80, 160, 288)]
+    sizes = [int(x * 1e9) for x in (0.1, 1, 7, 13, 34, 70, 175, 530)]
+    for nd in (1, 2, 8, 64):
+        for u in budgets:
+            st = [O.choose_stage(O.partition_plan(n, nd), u) for n in sizes]
+            keys = [(s, o) for s, o, _ in st]
+            assert keys == sorted(keys)
+        for n in sizes:
+            st = [O.choose_stage(O.partition_plan(n, nd), u)[:2] for u in budgets]
+            assert st == sorted(st, reverse=True)
+    for n in sizes:
+        for u in budgets:
+            st = [O.choose_stage(O.partition_plan(n, nd), u)[:2] for nd in (1, 2, 4, 8, 16, 64)]
+            assert st == sorted(st, reverse=True)

@@ -16,10 +16,11 @@ import os
 import torch  # noqa: F401  (loaded first so the library binds to the HIP runtime torch uses)
 
 __all__ = [
-    "ZeroError", "ZeroPlan", "ZeroAdamHParams", "ZeroAdamScalars", "lib", "lib_path",
+    "ZeroError", "ZeroPlan", "ZeroAdamHParams", "ZeroAdamScalars", "ZeroStageChoice", "lib", "lib_path",
     "ZERO_MAX_REPLICAS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
     "ZERO_ADAMW", "ZERO_ADAM_L2", "adam_hparams",
-    "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_adam_derive",
+    "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_choose_stage",
+    "zero_adam_derive",
     "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
     "zero_status_str", "zero_last_error",
 ]
@@ -59,6 +60,11 @@ class ZeroAdamHParams(ctypes.Structure):
                 ("wd_mode", ctypes.c_int32), ("reserved", ctypes.c_int32), ("step", ctypes.c_int64)]
 
 
+class ZeroStageChoice(ctypes.Structure):
+    _fields_ = [("stage", ctypes.c_uint32), ("offload_advised", ctypes.c_uint32),
+                ("bytes", ctypes.c_uint64 * 4)]
+
+
 class ZeroAdamScalars(ctypes.Structure):
     _fields_ = [(k, ctypes.c_float) for k in ("b1", "b2", "c1", "c2", "ss", "bc", "e", "dec", "w")]
 
@@ -91,6 +97,7 @@ def lib() -> ctypes.CDLL:
             "zero_partition_plan": [u64, u32, u32, P(ZeroPlan)],
             "zero_shard_range": [P(ZeroPlan), u32, P(u64), P(u64)],
             "zero_stage_bytes": [P(ZeroPlan), u32, u32, u32, u32, P(u64)],
+            "zero_choose_stage": [P(ZeroPlan), u64, u32, u32, u32, P(ZeroStageChoice)],
             "zero_adam_derive": [P(ZeroAdamHParams), P(ZeroAdamScalars)],
             "zero_reduce_shard": [P(_GradSrc), u64, vp, vp, vp, ctypes.c_double, vp],
             "zero_shard_sqnorm": [vp, u64, ctypes.c_double, vp, vp, vp],
@@ -145,6 +152,15 @@ def zero_stage_bytes(plan: ZeroPlan, stage: int, param_b: int = 2, grad_b: int =
     _check(lib().zero_stage_bytes(ctypes.byref(plan), stage, param_b, grad_b, opt_b, out),
            "zero_stage_bytes")
     return tuple(int(x) for x in out)
+
+
+def zero_choose_stage(plan: ZeroPlan, usable_bytes: int, param_b: int = 2, grad_b: int = 2,
+                      opt_b: int = 12) -> tuple[int, bool, tuple[int, int, int, int]]:
+    """(stage 1..3, offload advised, the stage's per-rank bytes) for a usable byte budget."""
+    out = ZeroStageChoice()
+    _check(lib().zero_choose_stage(ctypes.byref(plan), usable_bytes, param_b, grad_b, opt_b,
+                                   ctypes.byref(out)), "zero_choose_stage")
+    return int(out.stage), bool(out.offload_advised), tuple(int(x) for x in out.bytes)
 
 
 def zero_adam_derive(hp: ZeroAdamHParams) -> ZeroAdamScalars:

@@ -101,6 +101,25 @@ zero_status zero_stage_bytes(const zero_plan* p, uint32_t stage, uint32_t param_
   return ok();
 }
 
+// Stage choice: "ZeRO 优化器的三个阶段深度对比", section 四 (the decision tree), read as the
+// smallest stage whose per-rank bytes fit the caller's usable budget.
+zero_status zero_choose_stage(const zero_plan* p, uint64_t usable_bytes, uint32_t param_b,
+                              uint32_t grad_b, uint32_t opt_b, zero_stage_choice* out) {
+  if (!p || !out) return fail(ZERO_E_INVAL, "zero_choose_stage: NULL argument");
+  uint64_t b[4];
+  for (uint32_t stage = 1; stage <= 3; ++stage) {
+    const zero_status s = zero_stage_bytes(p, stage, param_b, grad_b, opt_b, b);
+    if (s != ZERO_OK) return s;
+    if (b[3] <= usable_bytes || stage == 3) {
+      out->stage = stage;
+      out->offload_advised = b[3] > usable_bytes ? 1u : 0u;
+      for (int i = 0; i < 4; ++i) out->bytes[i] = b[i];
+      return ok();
+    }
+  }
+  return fail(ZERO_E_INVAL, "zero_choose_stage: unreachable");
+}
+
 // The fp32 constants of one Adam step, each rounded once from fp64 (Kingma-Ba bias correction;
 // the pages name Adam and its state but print no equations).
 zero_status zero_adam_derive(const zero_adam_hparams* hp, zero_adam_scalars* out) {

@@ -11,7 +11,8 @@ Prints one JSON line (see the fields below). Flags:
   --gpus N         only 1 is supported: this path runs on one GPU's shard
   --steps K        timed steps (default 20)
   --warmup W       untimed steps first (default 3)
-  --workload NAME  llama7b (default), gpt2, llama13b (two-pass clip path), gpt3 (64 Mi windows)
+  --workload NAME  llama7b (default), gpt2, llama13b (two-pass clip path), gpt3 (64 Mi windows),
+                   gather7b (ZeRO-3: every Llama-7B layer gathered from its 8 rank shards)
   --cpu-seconds S  budget of the oracle's CPU baseline (default 12; 0 skips it)
   --copy-calib MB  also run a plain device copy of MB MiB 5 times (for counter calibration)
   --summarize      (no GPU) turn the rocprofv3 CSVs of the profile commands into the summaries
@@ -51,7 +52,10 @@ WL_DESC = {
                 "16 fp16 replicas x 2^16, two-pass clip path",
     "gpt3": "GPT-3-175B-shaped flat space (174,604,259,328 params), Nd=64, rank 0 shard, "
             "64 bf16 replicas per 64 Mi window",
+    "gather7b": "ZeRO-3 parameter gather: the 34 layers of the Llama-7B-shaped bf16 parameters "
+                "(6,738,415,616) rebuilt in turn from 8 rank shards",
 }
+GATHER_LAYERS = 34          # embeddings, 32 blocks, final norm + head
 
 
 def log(msg):
@@ -70,12 +74,16 @@ def _rb(w) -> int:
 
 def dominant_kernels(workload: str) -> list:
     """Library kernels of one step, the one that moves the most bytes first."""
+    if workload == "gather7b":
+        return ["k_gather"]
     return ["k_reduce", "k_adam_step"] if workload == "llama13b" else ["k_adam_step"]
 
 
 def kernel_bytes_per_elem(workload: str) -> dict:
     """Algorithmic HBM bytes each library kernel must move per shard element."""
     from workloads import WORKLOADS
+    if workload == "gather7b":
+        return {"k_gather": 2 + 2}            # each bf16 parameter read from its shard and written
     w = WORKLOADS[workload]
     if workload == "llama13b":
         # pass 1 reads R replicas and writes the fp32 gradient; pass 2 reads it, reads and
@@ -90,8 +98,10 @@ def shard_elems(w) -> int:
 
 
 def launch_elems(workload: str) -> int:
-    """Shard elements one launch of the dominant kernel covers."""
+    """Shard elements one launch of the dominant kernel covers (the mean, for the layer gather)."""
     from workloads import WORKLOADS
+    if workload == "gather7b":
+        return WORKLOADS["llama7b"].n // GATHER_LAYERS
     w = WORKLOADS[workload]
     return min(shard_elems(w), w.window or shard_elems(w))
 
@@ -274,6 +284,37 @@ def setup(name: str):
     return state
 
 
+def setup_gather():
+    import torch
+
+    import zero_partition_plan_amd as Z
+    from workloads import WORKLOADS, layer_ranges
+
+    w = WORKLOADS["llama7b"]
+    plan = Z.zero_partition_plan(w.n, w.nd)
+    S = plan.shard_elems
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(21)
+    flat = torch.randn(plan.padded_n, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    layers = layer_ranges("llama-7b")
+    assert len(layers) == GATHER_LAYERS
+    biggest = max(e - s for _, s, e in layers)
+    log(f"workload gather7b: {len(layers)} layers, largest {biggest}, S={S}")
+    st = dict(w=w, S=w.n, flat=flat, shards=[flat[r * S:(r + 1) * S] for r in range(w.nd)],
+              layers=layers, bufs=[torch.empty(biggest, dtype=torch.bfloat16, device=dev) for _ in range(2)],
+              t=1)
+    torch.cuda.synchronize()
+    return st
+
+
+def step_gather(st, spans):
+    """One ZeRO-3 forward's worth of gathers: every layer in order, alternating two buffers."""
+    import zero_partition_plan_amd as Z
+    for i, (_, a, b) in enumerate(st["layers"]):
+        spans("k_gather", lambda: Z.zero_gather_params(st["shards"], a, b - a, st["bufs"][i % 2]))
+
+
 def hparams(st):
     import zero_partition_plan_amd as Z
     w = st["w"]
@@ -380,7 +421,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama7b", choices=["llama7b", "gpt2", "llama13b", "gpt3"])
+    ap.add_argument("--workload", default="llama7b",
+                    choices=["llama7b", "gpt2", "llama13b", "gpt3", "gather7b"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calib", type=int, default=0)
     ap.add_argument("--summarize", action="store_true")
@@ -408,8 +450,11 @@ def main(argv=None):
     torch.cuda.set_device(0)
     log(f"kernel source sha256[:16] {kernel_hash()}")
 
-    st = setup(args.workload)
-    step = step_two_pass if args.workload == "llama13b" else step_fused
+    if args.workload == "gather7b":
+        st, step = setup_gather(), step_gather
+    else:
+        st = setup(args.workload)
+        step = step_two_pass if args.workload == "llama13b" else step_fused
     w, S = st["w"], st["S"]
 
     for _ in range(args.warmup):
@@ -445,7 +490,8 @@ def main(argv=None):
             f"{per_kernel[k]['median_ms']:.4f}, min {per_kernel[k]['min_ms']:.4f}, p90 "
             f"{per_kernel[k]['p90_ms']:.4f} -> {per_kernel[k]['gbs_at_avg']:.0f} GB/s")
     log(f"{args.steps} steps: {total_ms:.3f} ms on events, {wall * 1e3:.3f} ms wall")
-    assert torch.isfinite(st["inp"]["master"][:1 << 20]).all()
+    if "inp" in st:
+        assert torch.isfinite(st["inp"]["master"][:1 << 20]).all()
 
     dom = kernels[0]
     achieved = per_kernel[dom]["gbs_at_avg"]
@@ -462,12 +508,13 @@ def main(argv=None):
         del src, dst
 
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and args.workload != "gather7b":
         log(f"cpu baseline: oracle for {args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(args.workload, args.cpu_seconds)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload != "gather7b" else
+        "ZeRO-3 layer gather params/s + achieved HBM GB/s vs peak (7B, Nd=8)",
         "value": params_per_s,
         "unit": "params/s",
         "n_gpus": 1,
@@ -477,9 +524,16 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if args.workload != "gather7b" else "bf16",
         "data": "synthetic (seeded device draws; model shapes only, no weights)",
-        "config": {
+        "config": ({
+            "workload": WL_DESC[args.workload],
+            "params_gathered_per_step": S,
+            "shards": w.nd,
+            "layers": GATHER_LAYERS,
+            "dtype": "bf16",
+            "launches_per_step": {k: v["launches"] // args.steps for k, v in per_kernel.items()},
+        } if args.workload == "gather7b" else {
             "workload": WL_DESC[args.workload],
             "shard_elems": S,
             "replicas": w.reps,
@@ -488,7 +542,7 @@ def main(argv=None):
             "optimizer": f"AdamW wd={w.weight_decay}",
             "first_timed_t": w.warm_steps + 1 + args.warmup,
             "launches_per_step": {k: v["launches"] // args.steps for k, v in per_kernel.items()},
-        },
+        }),
         "roofline": {
             "bound": "hbm",
             "kernel": dom,

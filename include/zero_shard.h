@@ -34,6 +34,7 @@ extern "C" {
 #endif
 
 #define ZERO_MAX_REPLICAS 64   /* gradient replicas one call can sum */
+#define ZERO_MAX_SHARDS 64     /* rank shards one gather can read */
 
 typedef enum {
   ZERO_OK = 0,
@@ -182,6 +183,21 @@ zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float gra
                                  float* master, float* m, float* v, const zero_adam_hparams* hp,
                                  void* out_param, int32_t out_dtype, const int32_t* d_skip,
                                  void* stream);
+
+/* ZeRO-3 parameter gather for one layer (P1 section 三; P2 ZeRO Stage 3; P3 core operations: with
+ * parameters sharded, a layer's full parameters are rebuilt from every rank's shard before it runs
+ * and the other ranks' parts are released afterwards). The gathered flat space is the nd shards of
+ * shard_elems elements laid end to end in rank order (rank r holds [r*S, (r+1)*S), as
+ * zero_partition_plan lays it out); d_out (device, count elements) receives its elements
+ * [begin, begin + count). d_shards is a host array of nd device pointers, one per rank's shard of
+ * elem_bytes-wide elements (2: 16-bit parameters, 4: fp32); only the shards the range touches are
+ * read and must be non-NULL. On one GPU the shards are local buffers; across GPUs this is where an
+ * all-gather would land. The bytes are copied unchanged. count == 0 enqueues nothing.
+ * Errors: NULL array or out, nd outside 1..ZERO_MAX_SHARDS, elem_bytes not 2 or 4, a range past
+ * nd*S, out overlapping a shard it reads -> ZERO_E_INVAL; sizes >= 2^64 -> ZERO_E_OVERFLOW. */
+zero_status zero_gather_params(const void* const* d_shards, uint32_t nd, uint64_t shard_elems,
+                               uint32_t elem_bytes, uint64_t begin, uint64_t count, void* d_out,
+                               void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* zero_status_str(zero_status s);

@@ -22,6 +22,7 @@ Modules:
   adam       replica sum, non-finite flag, squared norm, clip coefficient,
              Adam/AdamW update and the full per-rank step                          [P1 二; P2 Stage 1/2]
   cast       fp32 -> bf16 / fp16 round-to-nearest-even (bit patterns as uint16)  [P1 一; P3 comparisons]
+  gather     ZeRO-3 gather of one layer's parameters from the rank shards         [P1 三; P3 core operations]
   memory     per-stage model-state bytes per rank (DP, ZeRO-1/2/3) and the
              stage-choice rule                                                  [P1 一/二/四; P3 stages]
 
@@ -43,6 +44,7 @@ from .adam import (
     sharded_step,
     unsharded_step,
 )
+from .gather import gather_range
 from .memory import MemoryEstimation, estimate_memory_per_gpu, stage_bytes_exact, STAGES, choose_stage
 
 __all__ = [
@@ -50,5 +52,6 @@ __all__ = [
     "cast_bf16_rne", "cast_fp16_rne", "widen_bf16", "widen_fp16",
     "AdamHParams", "AdamScalars", "adam_scalars", "adam_update", "replica_sum",
     "nonfinite_flag", "shard_sqnorm", "clip_coefficient", "sharded_step", "unsharded_step",
+    "gather_range",
     "MemoryEstimation", "estimate_memory_per_gpu", "stage_bytes_exact", "STAGES", "choose_stage",
 ]

@@ -18,6 +18,7 @@ from .shapes import (
     flat_count,
     param_list,
     init_ranges,
+    layer_ranges,
 )
 
-__all__ = ["MODELS", "WORKLOADS", "Workload", "flat_count", "param_list", "init_ranges"]
+__all__ = ["MODELS", "WORKLOADS", "Workload", "flat_count", "param_list", "init_ranges", "layer_ranges"]

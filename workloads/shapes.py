@@ -82,6 +82,29 @@ def flat_count(model: str) -> int:
     return sum(n for _, n, _ in param_list(model))
 
 
+def _layer_key(name: str) -> str:
+    head = name.split(".")[0]
+    if head[0] in "hl" and head[1:].isdigit():
+        return head                          # a transformer block
+    return "embed" if head in ("wte", "wpe", "embed") else "final"
+
+
+@lru_cache(maxsize=None)
+def layer_ranges(model: str) -> tuple:
+    """((layer, start, end), ...): consecutive flat ranges of the embeddings, each block, and the
+    final norm / head, in flattening order (the unit a ZeRO-3 forward gathers at a time)."""
+    out = []
+    pos = 0
+    for name, n, _ in param_list(model):
+        key = _layer_key(name)
+        if out and out[-1][0] == key:
+            out[-1] = (key, out[-1][1], pos + n)
+        else:
+            out.append((key, pos, pos + n))
+        pos += n
+    return tuple(out)
+
+
 @lru_cache(maxsize=None)
 def init_ranges(model: str) -> tuple:
     """((start, end, kind), ...) over the flat space, only the non-"normal" ranges, merged."""

@@ -17,15 +17,17 @@ import torch  # noqa: F401  (loaded first so the library binds to the HIP runtim
 
 __all__ = [
     "ZeroError", "ZeroPlan", "ZeroAdamHParams", "ZeroAdamScalars", "ZeroStageChoice", "lib", "lib_path",
-    "ZERO_MAX_REPLICAS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
+    "ZERO_MAX_REPLICAS", "ZERO_MAX_SHARDS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
     "ZERO_ADAMW", "ZERO_ADAM_L2", "adam_hparams",
     "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_choose_stage",
     "zero_adam_derive",
     "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
+    "zero_gather_params",
     "zero_status_str", "zero_last_error",
 ]
 
 ZERO_MAX_REPLICAS = 64
+ZERO_MAX_SHARDS = 64
 ZERO_OK, ZERO_E_INVAL, ZERO_E_OVERFLOW, ZERO_E_UNSUPPORTED, ZERO_E_HIP = range(5)
 ZERO_F32, ZERO_F16, ZERO_BF16 = 0, 1, 2
 ZERO_ADAMW, ZERO_ADAM_L2 = 0, 1
@@ -103,6 +105,7 @@ def lib() -> ctypes.CDLL:
             "zero_shard_sqnorm": [vp, u64, ctypes.c_double, vp, vp, vp],
             "zero_adam_shard_step": [P(_GradSrc), u64, ctypes.c_float, vp, vp, vp,
                                      P(ZeroAdamHParams), vp, i32, vp, vp],
+            "zero_gather_params": [P(vp), u32, u64, u32, u64, u64, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -240,3 +243,35 @@ def zero_adam_shard_step(reps, n: int, grad_scale: float, master, m, v, hp: Zero
         _ptr(m, n, "m", f32), _ptr(v, n, "v", f32), ctypes.byref(hp),
         _ptr(out, n, "out"), out_dt, _ptr(skip, 1, "skip", (torch.int32,)), _stream(stream)),
         "zero_adam_shard_step")
+
+
+def zero_gather_params(shards, begin: int, count: int, out, stream=None):
+    """out[:count] = the rank shards laid end to end, elements [begin, begin + count).
+
+    ``shards``: list of equally sized 1-D device tensors (one per rank; 16-bit or fp32), or a 2-D
+    tensor whose rows are the shards. Shards the range does not touch may be None.
+    """
+    rows = list(shards.unbind(0)) if isinstance(shards, torch.Tensor) and shards.dim() == 2 else list(shards)
+    if not rows or len(rows) > ZERO_MAX_SHARDS:
+        raise ValueError(f"1..{ZERO_MAX_SHARDS} shards")
+    ref = next((r for r in rows if r is not None), None)
+    if ref is None:
+        raise ValueError("every shard is None")
+    S, dt = ref.numel(), ref.dtype
+    eb = {torch.float16: 2, torch.bfloat16: 2, torch.int16: 2, torch.float32: 4, torch.int32: 4}.get(dt)
+    if eb is None:
+        raise TypeError(f"shard dtype {dt} is not a 2- or 4-byte type")
+    ptrs = []
+    for k, r in enumerate(rows):
+        if r is None:
+            ptrs.append(None)
+            continue
+        if r.dtype != dt or r.numel() != S:
+            raise ValueError("shards must share one dtype and length")
+        ptrs.append(_ptr(r, S, f"shard {k}"))
+    if out is not None and out.element_size() != eb:
+        raise TypeError("out must have the shards' element size")
+    arr = (ctypes.c_void_p * len(rows))(*ptrs)
+    _check(lib().zero_gather_params(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), len(rows), S, eb,
+                                    begin, count, _ptr(out, count, "out"), _stream(stream)),
+           "zero_gather_params")

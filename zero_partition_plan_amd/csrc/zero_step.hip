@@ -15,13 +15,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "zero_device.h"
 #include "zero_internal.h"
 
 #ifndef ZERO_ADAM_SUB
 #define ZERO_ADAM_SUB 2            // 4-element groups per thread per tile in the Adam kernel
-#endif
-#ifndef ZERO_NT
-#define ZERO_NT 1                  // streaming (non-temporal) loads and stores: data is touched once
 #endif
 #ifndef ZERO_ADAM_BLOCK
 #define ZERO_ADAM_BLOCK 64         // threads per block of the Adam kernel (one wave)
@@ -41,9 +39,11 @@ constexpr int kBlock = 256;            // reduce / squared-norm kernels
 constexpr int kWaves = kBlock / 64;
 constexpr int kAdamBlock = ZERO_ADAM_BLOCK;
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+using zero::f32x2;
+using zero::f32x4;
+using zero::ld;
+using zero::st;
+using zero::u32x2;
 
 struct RepPtrs {
   const void* p[ZERO_MAX_REPLICAS];
@@ -55,25 +55,7 @@ struct StepScalars {
 };
 
 // ---------------------------------------------------------------------------------------------
-// memory helpers
-
-template <typename T>
-__device__ __forceinline__ T ld(const T* p) {
-#if ZERO_NT
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
-
-template <typename T>
-__device__ __forceinline__ void st(T* p, T v) {
-#if ZERO_NT
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
-}
+// element conversions
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 

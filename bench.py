@@ -12,7 +12,8 @@ Prints one JSON line (see the fields below). Flags:
   --steps K        timed steps (default 20)
   --warmup W       untimed steps first (default 3)
   --workload NAME  llama7b (default), gpt2, llama13b (two-pass clip path), gpt3 (64 Mi windows),
-                   gather7b (ZeRO-3: every Llama-7B layer gathered from its 8 rank shards)
+                   gather7b (ZeRO-3: every Llama-7B layer gathered from its 8 rank shards),
+                   offload7b (ZeRO-Offload: the 7B shard's Adam state in host memory)
   --cpu-seconds S  budget of the oracle's CPU baseline (default 12; 0 skips it)
   --copy-calib MB  also run a plain device copy of MB MiB 5 times (for counter calibration)
   --summarize      (no GPU) turn the rocprofv3 CSVs of the profile commands into the summaries
@@ -54,8 +55,12 @@ WL_DESC = {
             "64 bf16 replicas per 64 Mi window",
     "gather7b": "ZeRO-3 parameter gather: the 34 layers of the Llama-7B-shaped bf16 parameters "
                 "(6,738,415,616) rebuilt in turn from 8 rank shards",
+    "offload7b": "ZeRO-Offload: Llama-7B-shaped shard (842,301,952 params, Nd=8, rank 0), 8 bf16 "
+                 "replicas summed on the GPU, AdamW on fp32 state in host memory, bf16 back to the slot",
 }
 GATHER_LAYERS = 34          # embeddings, 32 blocks, final norm + head
+OFFLOAD_CHUNK = 32 << 20    # elements per pipeline chunk
+OFFLOAD_THREADS = 16        # host threads (the machine's CPU share for one GPU)
 
 
 def log(msg):
@@ -76,6 +81,8 @@ def dominant_kernels(workload: str) -> list:
     """Library kernels of one step, the one that moves the most bytes first."""
     if workload == "gather7b":
         return ["k_gather"]
+    if workload == "offload7b":
+        return ["k_reduce"]
     return ["k_reduce", "k_adam_step"] if workload == "llama13b" else ["k_adam_step"]
 
 
@@ -84,6 +91,8 @@ def kernel_bytes_per_elem(workload: str) -> dict:
     from workloads import WORKLOADS
     if workload == "gather7b":
         return {"k_gather": 2 + 2}            # each bf16 parameter read from its shard and written
+    if workload == "offload7b":
+        return {"k_reduce": 8 * 2 + 4}        # 8 bf16 replicas in, the fp32 gradient chunk out
     w = WORKLOADS[workload]
     if workload == "llama13b":
         # pass 1 reads R replicas and writes the fp32 gradient; pass 2 reads it, reads and
@@ -102,6 +111,8 @@ def launch_elems(workload: str) -> int:
     from workloads import WORKLOADS
     if workload == "gather7b":
         return WORKLOADS["llama7b"].n // GATHER_LAYERS
+    if workload == "offload7b":
+        return OFFLOAD_CHUNK
     w = WORKLOADS[workload]
     return min(shard_elems(w), w.window or shard_elems(w))
 
@@ -315,6 +326,70 @@ def step_gather(st, spans):
         spans("k_gather", lambda: Z.zero_gather_params(st["shards"], a, b - a, st["bufs"][i % 2]))
 
 
+def setup_offload():
+    import torch
+
+    import zero_partition_plan_amd as Z
+    from workloads import WORKLOADS
+    from workloads import device as D
+
+    w = WORKLOADS["llama7b"]
+    plan = Z.zero_partition_plan(w.n, w.nd)
+    begin, valid = Z.zero_shard_range(plan, w.ranks[0])
+    S = plan.shard_elems
+    dev = torch.device("cuda:0")
+    inp = D.rank_inputs(w, begin, S, valid, device=dev)
+    host = {k: inp[k].cpu().numpy() for k in ("master", "m", "v")}   # the state lives on the host
+    del inp["master"], inp["m"], inp["v"]
+    torch.cuda.empty_cache()
+    log(f"workload offload7b: S={S}, host state {3 * 4 * S / 1e9:.1f} GB, chunk {OFFLOAD_CHUNK}")
+    st = dict(w=w, S=S, reps=inp["reps"], host=host, t=w.warm_steps + 1,
+              slot=torch.zeros(S, dtype=torch.bfloat16, device=dev),
+              bufs=Z.offload_buffers(OFFLOAD_CHUNK, threads=OFFLOAD_THREADS))
+    torch.cuda.synchronize()
+    return st
+
+
+def step_offload(st, spans):
+    import zero_partition_plan_amd as Z
+    h = st["host"]
+    spans("offload", lambda: Z.zero_offload_step(st["reps"], st["S"], 1.0, h["master"], h["m"], h["v"],
+                                                 hparams(st), st["slot"], st["bufs"]))
+    st["t"] += 1
+
+
+def offload_parts(st):
+    """Rates of the offloaded step's parts measured alone: host update, D2H, H2D (one chunk)."""
+    import torch
+
+    import zero_partition_plan_amd as Z
+    C, h, b = OFFLOAD_CHUNK, st["host"], st["bufs"]
+    out = torch.empty(C, dtype=torch.int16, pin_memory=True)
+    t0 = time.perf_counter()
+    for _ in range(3):
+        Z.zero_host_adam_step(b["h_grad"], C, 1.0, h["master"][:C], h["m"][:C], h["v"][:C], hparams(st),
+                              out=out, threads=OFFLOAD_THREADS)
+    host_s = (time.perf_counter() - t0) / 3
+    e0, e1 = new_event(), new_event()
+    e0.record()
+    for _ in range(3):
+        b["h_grad"][:C].copy_(b["d_grad"][:C], non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    d2h_ms = e0.elapsed_time(e1) / 3
+    e0.record()
+    for _ in range(3):
+        st["slot"][:C].view(torch.int16).copy_(b["h_param"][:C], non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    h2d_ms = e0.elapsed_time(e1) / 3
+    return {"chunk_elems": C, "host_threads": OFFLOAD_THREADS,
+            "host_update_gbs": 30 * C / host_s / 1e9, "host_update_params_per_s": C / host_s,
+            "d2h_gbs": 4 * C / d2h_ms / 1e6, "h2d_gbs": 2 * C / h2d_ms / 1e6,
+            "note": "host update moves 30 B per element in host memory (grad 4 + state 12 read, "
+                    "state 12 + bf16 2 written); d2h copies the fp32 gradient, h2d the bf16 parameters"}
+
+
 def hparams(st):
     import zero_partition_plan_amd as Z
     w = st["w"]
@@ -422,7 +497,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "gpt2", "llama13b", "gpt3", "gather7b"])
+                    choices=["llama7b", "gpt2", "llama13b", "gpt3", "gather7b", "offload7b"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calib", type=int, default=0)
     ap.add_argument("--summarize", action="store_true")
@@ -452,6 +527,8 @@ def main(argv=None):
 
     if args.workload == "gather7b":
         st, step = setup_gather(), step_gather
+    elif args.workload == "offload7b":
+        st, step = setup_offload(), step_offload
     else:
         st = setup(args.workload)
         step = step_two_pass if args.workload == "llama13b" else step_fused
@@ -480,6 +557,16 @@ def main(argv=None):
     bpe = kernel_bytes_per_elem(args.workload)
     n_launch = launch_elems(args.workload)
     per_kernel = {}
+    parts = None
+    if args.workload == "offload7b":
+        # the reduce kernel runs inside the offloaded call; time it alone on one chunk
+        import zero_partition_plan_amd as Z
+        d_g = st["bufs"]["d_grad"]
+        for _ in range(10):
+            spans("k_reduce", lambda: Z.zero_reduce_shard([r[:OFFLOAD_CHUNK] for r in st["reps"]],
+                                                          OFFLOAD_CHUNK, d_g))
+        torch.cuda.synchronize()
+        parts = offload_parts(st)
     for k in kernels:
         xs = spans.ms(k)
         per_kernel[k] = {"launches": len(xs), "avg_ms": sum(xs) / len(xs), "median_ms": pct(xs, 0.5),
@@ -508,13 +595,14 @@ def main(argv=None):
         del src, dst
 
     cpu = None
-    if args.cpu_seconds > 0 and args.workload != "gather7b":
+    if args.cpu_seconds > 0 and args.workload not in ("gather7b", "offload7b"):
         log(f"cpu baseline: oracle for {args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(args.workload, args.cpu_seconds)
 
     line = {
-        "metric": METRIC if args.workload != "gather7b" else
-        "ZeRO-3 layer gather params/s + achieved HBM GB/s vs peak (7B, Nd=8)",
+        "metric": {"gather7b": "ZeRO-3 layer gather params/s + achieved HBM GB/s vs peak (7B, Nd=8)",
+                   "offload7b": "ZeRO-Offload sharded Adam step params/s (7B, Nd=8, host-resident state)"
+                   }.get(args.workload, METRIC),
         "value": params_per_s,
         "unit": "params/s",
         "n_gpus": 1,
@@ -541,7 +629,8 @@ def main(argv=None):
             "param_out_dtype": w.out_dtypes[0],
             "optimizer": f"AdamW wd={w.weight_decay}",
             "first_timed_t": w.warm_steps + 1 + args.warmup,
-            "launches_per_step": {k: v["launches"] // args.steps for k, v in per_kernel.items()},
+            "launches_per_step": ({"k_reduce": -(-S // OFFLOAD_CHUNK)} if args.workload == "offload7b"
+                                  else {k: v["launches"] // args.steps for k, v in per_kernel.items()}),
         }),
         "roofline": {
             "bound": "hbm",
@@ -558,6 +647,8 @@ def main(argv=None):
         },
         "cpu_baseline": cpu,
     }
+    if parts is not None:
+        line["offload"] = parts
     print(json.dumps(line), flush=True)
     return 0
 

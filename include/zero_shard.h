@@ -199,6 +199,44 @@ zero_status zero_gather_params(const void* const* d_shards, uint32_t nd, uint64_
                                uint32_t elem_bytes, uint64_t begin, uint64_t count, void* d_out,
                                void* stream);
 
+/* The host half of ZeRO-Offload (P2 ZeRO-Offload: the optimizer state lives in host memory and the
+ * CPU updates it): one Adam/AdamW step on host arrays, with exactly the arithmetic, operation order
+ * and rounding of zero_adam_shard_step (so both give the same bits), on the fp32 gradient grad
+ * (host float[n]) times grad_scale; master, m, v (host float[n]) are updated in place and
+ * out_param (host, nullable) receives the bf16/fp16 round-to-nearest-even parameters. threads: host
+ * threads to split the range over (0 = all hardware threads). Synchronous; no HIP calls.
+ * Errors: NULLs, bad hparams, overlapping arrays -> ZERO_E_INVAL; out dtype fp32 ->
+ * ZERO_E_UNSUPPORTED; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
+zero_status zero_host_adam_step(const float* grad, uint64_t n, float grad_scale, float* master,
+                                float* m, float* v, const zero_adam_hparams* hp, void* out_param,
+                                int32_t out_dtype, uint32_t threads);
+
+/* Staging for zero_offload_step, allocated by the caller. */
+typedef struct {
+  float* d_grad;        /* device float[2 * chunk_elems]: reduced-gradient chunks */
+  float* h_grad;        /* pinned host float[2 * chunk_elems]: their copies */
+  void* h_param;        /* pinned host 16-bit [2 * chunk_elems]: updated parameters */
+  uint64_t chunk_elems; /* pipeline chunk, >= 1 */
+  uint32_t threads;     /* host threads for the update (0 = all) */
+  uint32_t reserved;
+  void* h2d_stream;     /* stream for the parameter copies back to the GPU (NULL = `stream`) */
+} zero_offload_buffers;
+
+/* One rank's offloaded step (P2 ZeRO-Offload): for each chunk of the shard, the GPU sums the
+ * gradient replicas (as zero_reduce_shard) and the chunk is copied to pinned host memory; the host
+ * runs zero_host_adam_step on its part of h_master/h_m/h_v (host float[n], updated in place) and
+ * the 16-bit parameters are copied into d_out_param (device, the rank's slot, out_dtype bf16 or
+ * fp16). Chunks are double-buffered: the GPU reduces and copies chunk c+1 while the host updates
+ * chunk c, and chunk c's parameters travel back on h2d_stream while the host works on the next.
+ * Results equal zero_adam_shard_step's bit for bit. Host-synchronous: returns once every parameter
+ * copy has landed; it creates and destroys four HIP events per call. Errors: as
+ * zero_host_adam_step and zero_reduce_shard, plus NULL or incomplete buffers -> ZERO_E_INVAL and
+ * HIP failures -> ZERO_E_HIP (the state may then be partly updated). */
+zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_scale,
+                              float* h_master, float* h_m, float* h_v, const zero_adam_hparams* hp,
+                              void* d_out_param, int32_t out_dtype,
+                              const zero_offload_buffers* buf, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* zero_status_str(zero_status s);
 

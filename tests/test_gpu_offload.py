@@ -1,0 +1,89 @@
+"""GPU + host parity of the offloaded step (ZeRO-Offload): device replica sum per chunk, copy to
+pinned host memory, host Adam on host state, 16-bit parameters copied into the device slot. Bit
+for bit against the oracle and against the all-device step on the same inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import zero_partition_plan_amd as Z
+from gpu_util import DEV, assert_bits_equal, banner, bits16, bits32, dev_rep, f32_bits
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def _inputs(rng, n, R):
+    x = rng.standard_normal((R, n)).astype(np.float32) * np.float32(1e-3)
+    reps = (x.view(np.uint32) >> 16).astype(np.uint16)
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (rng.random(n) * 1e-7).astype(np.float32)
+    return reps, master, m, v
+
+
+@pytest.mark.parametrize("n,chunk,side", [(5 * 4096 + 777, 4096, False), (5 * 4096 + 777, 4096, True),
+                                          (1000, 4096, False), (1, 1, True), (3 * 65536, 65536, True),
+                                          (64 << 20, 8 << 20, True)])
+def test_offload_step_matches_oracle_and_device_step(n, chunk, side):
+    banner(f"offload n={n} chunk={chunk} side={side}")
+    rng = np.random.default_rng(n % 997 + chunk)
+    R = 8
+    reps, master, m, v = _inputs(rng, n, R)
+    d_reps = dev_rep(reps.reshape(-1), "bf16").view(R, n)
+    hp = Z.adam_hparams(step=4, **HP)
+    # offloaded: host state, device slot
+    hm, hmm, hv = master.copy(), m.copy(), v.copy()
+    slot = torch.full((n + 8,), -1.0, dtype=torch.bfloat16, device=DEV)
+    stream = torch.cuda.Stream() if side else None
+    bufs = Z.offload_buffers(chunk, threads=8, h2d_stream=stream)
+    Z.zero_offload_step(d_reps, n, 0.5, hm, hmm, hv, hp, slot[4:4 + n], bufs)
+    torch.cuda.synchronize()
+    got_slot = bits16(slot)
+    assert (got_slot[:4] == got_slot[0]).all() and (got_slot[4 + n:] == got_slot[0]).all()
+    # oracle
+    p2, m2, v2, o2 = O.sharded_step(list(reps), "bf16", 0.5, master, m, v, O.AdamHParams(step=4, **HP), "bf16")
+    assert_bits_equal(hm.view(np.uint32), f32_bits(p2), "host master")
+    assert_bits_equal(hmm.view(np.uint32), f32_bits(m2), "host m")
+    assert_bits_equal(hv.view(np.uint32), f32_bits(v2), "host v")
+    assert_bits_equal(got_slot[4:4 + n], o2, "slot")
+    # the all-device step on the same inputs gives the same bits
+    dp, dm, dv = (torch.from_numpy(a.copy()).to(DEV) for a in (master, m, v))
+    dslot = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    Z.zero_adam_shard_step(d_reps, n, 0.5, dp, dm, dv, hp, out=dslot)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits32(dp), hm.view(np.uint32), "device vs host master")
+    assert_bits_equal(bits16(dslot), got_slot[4:4 + n], "device vs host slot")
+
+
+def test_offload_fp16_slot_and_l2_mode():
+    rng = np.random.default_rng(3)
+    n, R = 3 * 5000 + 3, 3
+    x = rng.standard_normal((R, n)).astype(np.float32) * np.float32(1e-3 * 1024)
+    reps = x.astype(np.float16).view(np.uint16)
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    z = np.zeros(n, np.float32)
+    kw = {**HP, "wd_mode": "l2", "weight_decay": 0.1, "step": 1}
+    hm, hmm, hv = master.copy(), z.copy(), z.copy()
+    slot = torch.zeros(n, dtype=torch.float16, device=DEV)
+    Z.zero_offload_step([dev_rep(r, "f16") for r in reps], n, 1.0 / 1024, hm, hmm, hv, Z.adam_hparams(**kw),
+                        slot, Z.offload_buffers(5000, threads=3))
+    torch.cuda.synchronize()
+    p2, m2, v2, o2 = O.sharded_step(list(reps), "f16", 1.0 / 1024, master, z, z, O.AdamHParams(**kw), "f16")
+    assert_bits_equal(hm.view(np.uint32), f32_bits(p2), "host master")
+    assert_bits_equal(bits16(slot), o2, "fp16 slot")
+
+
+def test_offload_rejects_bad_buffers():
+    n = 100
+    d_rep = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    h = [np.zeros(n, np.float32) for _ in range(3)]
+    slot = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    bufs = Z.offload_buffers(64)
+    bufs["chunk_elems"] = 0
+    with pytest.raises((Z.ZeroError, ValueError)):
+        Z.zero_offload_step([d_rep], n, 1.0, *h, Z.adam_hparams(), slot, bufs)
+    with pytest.raises(Z.ZeroError):                  # host state aliasing
+        Z.zero_offload_step([d_rep], n, 1.0, h[0], h[0], h[2], Z.adam_hparams(), slot, Z.offload_buffers(64))

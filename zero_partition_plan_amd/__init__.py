@@ -16,13 +16,14 @@ import os
 import torch  # noqa: F401  (loaded first so the library binds to the HIP runtime torch uses)
 
 __all__ = [
-    "ZeroError", "ZeroPlan", "ZeroAdamHParams", "ZeroAdamScalars", "ZeroStageChoice", "lib", "lib_path",
+    "ZeroError", "ZeroPlan", "ZeroAdamHParams", "ZeroAdamScalars", "ZeroStageChoice",
+    "ZeroOffloadBuffers", "lib", "lib_path", "offload_buffers",
     "ZERO_MAX_REPLICAS", "ZERO_MAX_SHARDS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
     "ZERO_ADAMW", "ZERO_ADAM_L2", "adam_hparams",
     "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_choose_stage",
     "zero_adam_derive",
     "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
-    "zero_gather_params",
+    "zero_gather_params", "zero_host_adam_step", "zero_offload_step",
     "zero_status_str", "zero_last_error",
 ]
 
@@ -67,6 +68,12 @@ class ZeroStageChoice(ctypes.Structure):
                 ("bytes", ctypes.c_uint64 * 4)]
 
 
+class ZeroOffloadBuffers(ctypes.Structure):
+    _fields_ = [("d_grad", ctypes.c_void_p), ("h_grad", ctypes.c_void_p), ("h_param", ctypes.c_void_p),
+                ("chunk_elems", ctypes.c_uint64), ("threads", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32), ("h2d_stream", ctypes.c_void_p)]
+
+
 class ZeroAdamScalars(ctypes.Structure):
     _fields_ = [(k, ctypes.c_float) for k in ("b1", "b2", "c1", "c2", "ss", "bc", "e", "dec", "w")]
 
@@ -106,6 +113,10 @@ def lib() -> ctypes.CDLL:
             "zero_adam_shard_step": [P(_GradSrc), u64, ctypes.c_float, vp, vp, vp,
                                      P(ZeroAdamHParams), vp, i32, vp, vp],
             "zero_gather_params": [P(vp), u32, u64, u32, u64, u64, vp, vp],
+            "zero_host_adam_step": [vp, u64, ctypes.c_float, vp, vp, vp, P(ZeroAdamHParams), vp, i32,
+                                    u32],
+            "zero_offload_step": [P(_GradSrc), u64, ctypes.c_float, vp, vp, vp, P(ZeroAdamHParams),
+                                  vp, i32, P(ZeroOffloadBuffers), vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -275,3 +286,62 @@ def zero_gather_params(shards, begin: int, count: int, out, stream=None):
     _check(lib().zero_gather_params(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), len(rows), S, eb,
                                     begin, count, _ptr(out, count, "out"), _stream(stream)),
            "zero_gather_params")
+
+
+# ------------------------------------------------------------------------------ host (offload) calls
+
+def _hptr(a, n: int, what: str, itemsize: int):
+    """Host array (numpy array or CPU torch tensor) -> address, checked for size and layout."""
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda:
+            raise TypeError(f"{what} must be host memory")
+        if not a.is_contiguous() or a.element_size() != itemsize:
+            raise ValueError(f"{what}: contiguous {itemsize}-byte elements expected")
+        if a.numel() < n:
+            raise ValueError(f"{what} holds {a.numel()} elements, {n} needed")
+        return a.data_ptr()
+    import numpy as np
+    if not isinstance(a, np.ndarray) or not a.flags["C_CONTIGUOUS"] or a.itemsize != itemsize:
+        raise ValueError(f"{what}: contiguous numpy array of {itemsize}-byte elements expected")
+    if a.size < n:
+        raise ValueError(f"{what} holds {a.size} elements, {n} needed")
+    return a.ctypes.data
+
+
+def zero_host_adam_step(grad, n: int, grad_scale: float, master, m, v, hp: ZeroAdamHParams,
+                        out=None, out_dtype: int = ZERO_BF16, threads: int = 0):
+    """The host update on host arrays (numpy or CPU tensors); ``out`` holds 16-bit patterns."""
+    _check(lib().zero_host_adam_step(
+        _hptr(grad, n, "grad", 4), n, float(grad_scale), _hptr(master, n, "master", 4),
+        _hptr(m, n, "m", 4), _hptr(v, n, "v", 4), ctypes.byref(hp), _hptr(out, n, "out", 2),
+        out_dtype, threads), "zero_host_adam_step")
+
+
+def offload_buffers(chunk_elems: int, device="cuda", threads: int = 0, h2d_stream=None) -> dict:
+    """Caller-side staging for zero_offload_step: device and pinned host chunk buffers (x2)."""
+    bufs = {
+        "d_grad": torch.empty(2 * chunk_elems, dtype=torch.float32, device=device),
+        "h_grad": torch.empty(2 * chunk_elems, dtype=torch.float32, pin_memory=True),
+        "h_param": torch.empty(2 * chunk_elems, dtype=torch.int16, pin_memory=True),
+        "chunk_elems": chunk_elems, "threads": threads, "h2d_stream": h2d_stream,
+    }
+    return bufs
+
+
+def zero_offload_step(reps, n: int, grad_scale: float, h_master, h_m, h_v, hp: ZeroAdamHParams,
+                      out, buffers: dict, stream=None):
+    """Offloaded step: device replicas -> host Adam on host state -> 16-bit params into ``out``."""
+    src, keep = _src(reps, n)
+    if out is None or out.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("out must be a bfloat16 or float16 device tensor")
+    C = int(buffers["chunk_elems"])
+    b = ZeroOffloadBuffers(_ptr(buffers["d_grad"], 2 * C, "d_grad", (torch.float32,)),
+                           _hptr(buffers["h_grad"], 2 * C, "h_grad", 4),
+                           _hptr(buffers["h_param"], 2 * C, "h_param", 2), C, int(buffers["threads"]), 0,
+                           None if buffers.get("h2d_stream") is None else _stream(buffers["h2d_stream"]))
+    _check(lib().zero_offload_step(
+        ctypes.byref(src), n, float(grad_scale), _hptr(h_master, n, "master", 4), _hptr(h_m, n, "m", 4),
+        _hptr(h_v, n, "v", 4), ctypes.byref(hp), _ptr(out, n, "out"), _TORCH_DT[out.dtype],
+        ctypes.byref(b), _stream(stream)), "zero_offload_step")

@@ -28,6 +28,7 @@ and their console output in the .log file of the same name.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -41,7 +42,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sharded Adam step params/s per GPU + achieved HBM GB/s vs peak (7B, Nd=8)"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "zero_partition_plan_amd", "csrc", "zero_step.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "zero_partition_plan_amd", "csrc", f)
+               for f in ("zero_step.hip", "zero_gather.hip", "zero_device.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 CALIB_MIB = 1024
 
@@ -50,7 +52,10 @@ WL_DESC = {
                "8 bf16 replicas, warm AdamW state",
     "gpt2": "GPT-2-small-shaped flat space (124,356,864 params), Nd=8, rank 3 shard, 8 bf16 replicas",
     "llama13b": "Llama-13B-shaped flat space (13,015,864,320 params), Nd=16, rank 5 shard, "
-                "16 fp16 replicas x 2^16, two-pass clip path",
+                "16 fp16 replicas x 2^16 with 0.01% +inf (every step overflows and is skipped), "
+                "two-pass clip path",
+    "llama13b-clean": "Llama-13B-shaped flat space (13,015,864,320 params), Nd=16, rank 5 shard, "
+                      "16 fp16 replicas x 2^16, no overflow, two-pass clip path",
     "gpt3": "GPT-3-175B-shaped flat space (174,604,259,328 params), Nd=64, rank 0 shard, "
             "64 bf16 replicas per 64 Mi window",
     "gather7b": "ZeRO-3 parameter gather: the 34 layers of the Llama-7B-shaped bf16 parameters "
@@ -68,7 +73,11 @@ def log(msg):
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """sha256[:16] over every device source: a counter summary is used only for this exact code."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 # ----------------------------------------------------------------------------- bytes
@@ -83,7 +92,7 @@ def dominant_kernels(workload: str) -> list:
         return ["k_gather"]
     if workload == "offload7b":
         return ["k_reduce"]
-    return ["k_reduce", "k_adam_step"] if workload == "llama13b" else ["k_adam_step"]
+    return ["k_reduce", "k_adam_step"] if workload.startswith("llama13b") else ["k_adam_step"]
 
 
 def kernel_bytes_per_elem(workload: str) -> dict:
@@ -93,8 +102,8 @@ def kernel_bytes_per_elem(workload: str) -> dict:
         return {"k_gather": 2 + 2}            # each bf16 parameter read from its shard and written
     if workload == "offload7b":
         return {"k_reduce": 8 * 2 + 4}        # 8 bf16 replicas in, the fp32 gradient chunk out
-    w = WORKLOADS[workload]
-    if workload == "llama13b":
+    w = WORKLOADS["llama13b" if workload.startswith("llama13b") else workload]
+    if workload.startswith("llama13b"):
         # pass 1 reads R replicas and writes the fp32 gradient; pass 2 reads it, reads and
         # writes master/m/v and writes the 16-bit parameters
         return {"k_reduce": w.reps * _rb(w) + 4, "k_adam_step": 4 + 24 + 2}
@@ -113,7 +122,7 @@ def launch_elems(workload: str) -> int:
         return WORKLOADS["llama7b"].n // GATHER_LAYERS
     if workload == "offload7b":
         return OFFLOAD_CHUNK
-    w = WORKLOADS[workload]
+    w = WORKLOADS["llama13b" if workload.startswith("llama13b") else workload]
     return min(shard_elems(w), w.window or shard_elems(w))
 
 
@@ -271,7 +280,9 @@ def setup(name: str):
     from workloads import WORKLOADS
     from workloads import device as D
 
-    w = WORKLOADS[name]
+    w = WORKLOADS["llama13b"] if name.startswith("llama13b") else WORKLOADS[name]
+    if name == "llama13b-clean":
+        w = dataclasses.replace(w, inf_rate=0.0)
     plan = Z.zero_partition_plan(w.n, w.nd)
     rank = w.ranks[0]
     begin, valid = Z.zero_shard_range(plan, rank)
@@ -281,14 +292,17 @@ def setup(name: str):
     inp = D.rank_inputs(w, begin, S, valid, device=dev, rep_size=w.window)
     out_t = torch.float16 if w.out_dtypes[0] == "f16" else torch.bfloat16
     state = dict(w=w, plan=plan, S=S, begin=begin, inp=inp, t=w.warm_steps + 1)
-    if w.window is None and name != "llama13b":
+    if w.window is None and not name.startswith("llama13b"):
         state["full"] = torch.zeros(plan.padded_n, dtype=out_t, device=dev)
         state["slot"] = state["full"][begin:begin + S]
     else:
         state["slot"] = torch.zeros(S, dtype=out_t, device=dev)
-    if name == "llama13b":
+    if name.startswith("llama13b"):
         state["g"] = torch.empty(S, device=dev)
         state["flag"] = torch.zeros(1, dtype=torch.int32, device=dev)
+        state["host_sq"] = torch.zeros(1, dtype=torch.float64, pin_memory=True)
+        state["host_flag"] = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+        state["skipped"] = 0
         state["parts"] = torch.empty(Z.zero_sq_partials_len(S), dtype=torch.float64, device=dev)
         state["sq"] = torch.empty(1, dtype=torch.float64, device=dev)
     torch.cuda.synchronize()
@@ -431,7 +445,14 @@ def step_fused(st, spans):
 
 
 def step_two_pass(st, spans):
-    """Reduce -> squared norm -> clip scale (host) -> AdamW with the device skip flag."""
+    """Reduce -> squared norm -> one 12-byte read of (norm, flag) -> clip scale on the host -> AdamW.
+
+    The host already waits for the squared norm to form the clip coefficient, so it reads the
+    overflow flag in the same copy and does not launch the update when it is set (t does not
+    advance). The update still gets the device flag, as a caller that does not read it back would.
+    """
+    import torch
+
     import zero_partition_plan_amd as Z
     w, inp, S = st["w"], st["inp"], st["S"]
     inv_ls = 1.0 / w.loss_scale
@@ -439,8 +460,14 @@ def step_two_pass(st, spans):
     spans("k_reduce", lambda: Z.zero_reduce_shard(inp["reps"], S, st["g"], st["flag"], st["parts"],
                                                   inv_ls))
     Z.zero_shard_sqnorm(None, S, inv_ls, st["parts"], st["sq"])
-    sq = float(st["sq"].item())                 # 8-byte device -> host read for the clip scale
-    coef = min(1.0, w.max_norm / (math.sqrt(sq) + 1e-6)) if math.isfinite(sq) else 1.0
+    st["host_sq"].copy_(st["sq"], non_blocking=True)
+    st["host_flag"].copy_(st["flag"], non_blocking=True)
+    torch.cuda.current_stream().synchronize()
+    sq, flag = float(st["host_sq"][0]), int(st["host_flag"][0])
+    if flag:
+        st["skipped"] += 1
+        return
+    coef = min(1.0, w.max_norm / (math.sqrt(sq) + 1e-6))
     spans("k_adam_step", lambda: Z.zero_adam_shard_step(
         [st["g"]], S, coef * inv_ls, inp["master"], inp["m"], inp["v"], hparams(st), out=st["slot"],
         skip=st["flag"]))
@@ -468,7 +495,7 @@ def cpu_baseline(name: str, seconds: float):
     from workloads import WORKLOADS
     from workloads import host as H
 
-    w = WORKLOADS[name]
+    w = WORKLOADS["llama13b" if name.startswith("llama13b") else name]
     win = 1 << 21
     plan = O.partition_plan(w.n, w.nd)
     begin, _ = O.shard_range(plan, w.ranks[0])
@@ -497,7 +524,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "gpt2", "llama13b", "gpt3", "gather7b", "offload7b"])
+                    choices=["llama7b", "gpt2", "llama13b", "llama13b-clean", "gpt3", "gather7b",
+                             "offload7b"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calib", type=int, default=0)
     ap.add_argument("--summarize", action="store_true")
@@ -531,7 +559,7 @@ def main(argv=None):
         st, step = setup_offload(), step_offload
     else:
         st = setup(args.workload)
-        step = step_two_pass if args.workload == "llama13b" else step_fused
+        step = step_two_pass if args.workload.startswith("llama13b") else step_fused
     w, S = st["w"], st["S"]
 
     for _ in range(args.warmup):
@@ -569,6 +597,10 @@ def main(argv=None):
         parts = offload_parts(st)
     for k in kernels:
         xs = spans.ms(k)
+        if not xs:                         # e.g. the update pass of steps that were all skipped
+            per_kernel[k] = {"launches": 0}
+            log(f"{k}: not launched")
+            continue
         per_kernel[k] = {"launches": len(xs), "avg_ms": sum(xs) / len(xs), "median_ms": pct(xs, 0.5),
                          "min_ms": min(xs), "p90_ms": pct(xs, 0.9),
                          "bytes_per_elem": bpe[k],
@@ -576,6 +608,8 @@ def main(argv=None):
         log(f"{k}: {len(xs)} launches, avg {per_kernel[k]['avg_ms']:.4f} ms, median "
             f"{per_kernel[k]['median_ms']:.4f}, min {per_kernel[k]['min_ms']:.4f}, p90 "
             f"{per_kernel[k]['p90_ms']:.4f} -> {per_kernel[k]['gbs_at_avg']:.0f} GB/s")
+    if "skipped" in st:
+        log(f"overflow-skipped steps: {st['skipped']} of {args.warmup + args.steps}")
     log(f"{args.steps} steps: {total_ms:.3f} ms on events, {wall * 1e3:.3f} ms wall")
     if "inp" in st:
         assert torch.isfinite(st["inp"]["master"][:1 << 20]).all()
@@ -630,7 +664,9 @@ def main(argv=None):
             "optimizer": f"AdamW wd={w.weight_decay}",
             "first_timed_t": w.warm_steps + 1 + args.warmup,
             "launches_per_step": ({"k_reduce": -(-S // OFFLOAD_CHUNK)} if args.workload == "offload7b"
-                                  else {k: v["launches"] // args.steps for k, v in per_kernel.items()}),
+                                  else {k: v["launches"] / args.steps for k, v in per_kernel.items()}),
+            **({"overflow_skipped_steps": st["skipped"], "counted_steps": args.warmup + args.steps}
+               if "skipped" in st else {}),
         }),
         "roofline": {
             "bound": "hbm",
@@ -643,7 +679,7 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": bpe[dom] * n_launch,
             "avg_launch_ms": per_kernel[dom]["avg_ms"],
             "launch_ms": {k: {q: round(v[q], 5) for q in ("median_ms", "min_ms", "p90_ms")}
-                          for k, v in per_kernel.items()},
+                          for k, v in per_kernel.items() if v["launches"]},
         },
         "cpu_baseline": cpu,
     }

@@ -276,11 +276,9 @@ __device__ __forceinline__ bool nonfinite(float x) {
 }
 
 template <int RDT, int RFIX, bool VEC>
-__global__ __launch_bounds__(64) void k_reduce(RepPtrs reps, int nrep, uint64_t first_tile,
-                                               uint64_t n, float* __restrict__ G,
-                                               int32_t* __restrict__ flag,
-                                               double* __restrict__ partials, double sq_scale) {
-  const uint64_t tile = first_tile + blockIdx.x;
+__device__ __forceinline__ void reduce_tile(const RepPtrs& reps, int nrep, uint64_t tile, uint64_t n,
+                                            float* __restrict__ G, int32_t* __restrict__ flag,
+                                            double* __restrict__ partials, double sq_scale) {
   const uint64_t base = tile * kRedTile;
   double sq = 0.0;
   bool bad = false;
@@ -318,6 +316,24 @@ __global__ __launch_bounds__(64) void k_reduce(RepPtrs reps, int nrep, uint64_t 
     sq = wave_sum(sq);
     if (threadIdx.x == 0) partials[tile] = sq;
   }
+}
+
+// whole, aligned tiles with vector loads
+template <int RDT, int RFIX>
+__global__ __launch_bounds__(64) void k_reduce(RepPtrs reps, int nrep, uint64_t first_tile,
+                                               uint64_t n, float* __restrict__ G,
+                                               int32_t* __restrict__ flag,
+                                               double* __restrict__ partials, double sq_scale) {
+  reduce_tile<RDT, RFIX, true>(reps, nrep, first_tile + blockIdx.x, n, G, flag, partials, sq_scale);
+}
+
+// the ragged last tile, or every tile of arrays that are not aligned: element by element
+template <int RDT>
+__global__ __launch_bounds__(64) void k_reduce_tail(RepPtrs reps, int nrep, uint64_t first_tile,
+                                                    uint64_t n, float* __restrict__ G,
+                                                    int32_t* __restrict__ flag,
+                                                    double* __restrict__ partials, double sq_scale) {
+  reduce_tile<RDT, 0, false>(reps, nrep, first_tile + blockIdx.x, n, G, flag, partials, sq_scale);
 }
 
 // level 1: block b sums partials [b*chunk, min(ntiles, (b+1)*chunk)) into partials[ntiles + b]
@@ -483,8 +499,12 @@ template <int RDT, int RFIX, bool VEC>
 void launch_reduce(const ReduceArgs& a, uint64_t t0, uint64_t t1) {
   for (uint64_t t = t0; t < t1; t += kMaxGrid) {
     const uint64_t g = t1 - t < kMaxGrid ? t1 - t : kMaxGrid;
-    hipLaunchKernelGGL((k_reduce<RDT, RFIX, VEC>), dim3((unsigned)g), dim3(64), 0, a.stream, a.reps,
-                       a.nrep, t, a.n, a.G, a.flag, a.partials, a.sq_scale);
+    if constexpr (VEC)
+      hipLaunchKernelGGL((k_reduce<RDT, RFIX>), dim3((unsigned)g), dim3(64), 0, a.stream, a.reps,
+                         a.nrep, t, a.n, a.G, a.flag, a.partials, a.sq_scale);
+    else
+      hipLaunchKernelGGL((k_reduce_tail<RDT>), dim3((unsigned)g), dim3(64), 0, a.stream, a.reps,
+                         a.nrep, t, a.n, a.G, a.flag, a.partials, a.sq_scale);
   }
 }
 

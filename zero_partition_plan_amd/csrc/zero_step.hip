@@ -6,8 +6,9 @@
 // or 512 B (16-bit) run. Loads and stores are non-temporal: every byte is touched once per step.
 // The Adam kernel runs one single-wave tile per block over the aligned whole tiles of the shard;
 // a separate per-element kernel takes the ragged end and arrays that are not 16-byte aligned.
-// Measured on MI355X, one-wave blocks with 2 groups per lane moved this 15-stream read/write mix
-// faster than 128- or 256-thread blocks and than grid-stride (persistent) launches.
+// Measured on MI355X, one-wave blocks with one group per lane (a 256-element tile) moved this
+// 15-stream read/write mix fastest: faster than 2 or 4 groups per lane, 128- or 256-thread blocks,
+// grid-stride (persistent) launches and software-pipelined multi-tile blocks.
 //
 // Arithmetic is fp32 with every operation rounded on its own: the library is built with
 // -ffp-contract=off and HIP's correctly rounded fp32 division and square root, so the results
@@ -15,11 +16,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "zero_device.h"
 #include "zero_internal.h"
 
 #ifndef ZERO_ADAM_SUB
-#define ZERO_ADAM_SUB 2            // 4-element groups per thread per tile in the Adam kernel
+#define ZERO_ADAM_SUB 1            // 4-element groups per thread per tile in the Adam kernel
 #endif
 #ifndef ZERO_ADAM_BLOCK
 #define ZERO_ADAM_BLOCK 64         // threads per block of the Adam kernel (one wave)
@@ -44,6 +47,18 @@ using zero::f32x4;
 using zero::ld;
 using zero::st;
 using zero::u32x2;
+
+// f(0), f(1), ..., f(N-1) with compile-time indices and no loop in the code. A loop that runs
+// once (N = 1) lets loop-invariant code motion promote its stores, and the promoted stores lose
+// their non-temporal hint before the loop would be unrolled.
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 struct RepPtrs {
   const void* p[ZERO_MAX_REPLICAS];
@@ -194,8 +209,7 @@ __global__ __launch_bounds__(kAdamBlock) ZERO_ADAM_WAVES_ATTR void k_adam_step(
     v[u] = ld(reinterpret_cast<const f32x4*>(V + idx[u]));
   }
   sum_reps4<RDT, RFIX, SUB>(reps, nrep, idx, acc);
-#pragma unroll
-  for (int u = 0; u < SUB; ++u) {
+  unroll<SUB>([&](auto u) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float pq = p[u][q], mq = m[u][q], vq = v[u][q];
@@ -208,12 +222,10 @@ __global__ __launch_bounds__(kAdamBlock) ZERO_ADAM_WAVES_ATTR void k_adam_step(
     st(reinterpret_cast<f32x4*>(M + idx[u]), m[u]);
     st(reinterpret_cast<f32x4*>(V + idx[u]), v[u]);
     if constexpr (ODT != ZERO_F32) {
-      u32x2 o;
-      o.x = pack2<ODT>(p[u].x, p[u].y);
-      o.y = pack2<ODT>(p[u].z, p[u].w);
+      const u32x2 o = {pack2<ODT>(p[u].x, p[u].y), pack2<ODT>(p[u].z, p[u].w)};
       st(reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx[u]), o);
     }
-  }
+  });
 }
 
 // elements [begin, n), one per thread per grid-stride iteration, any alignment

@@ -27,6 +27,9 @@
 #ifndef ZERO_ADAM_BLOCK
 #define ZERO_ADAM_BLOCK 64         // threads per block of the Adam kernel (one wave)
 #endif
+#ifndef ZERO_REP_BATCH
+#define ZERO_REP_BATCH 8           // replica loads issued together before they are summed
+#endif
 #ifndef ZERO_ADAM_WAVES
 #define ZERO_ADAM_WAVES 0          // > 0: ask for at least this many waves per SIMD (register cap)
 #endif
@@ -135,19 +138,20 @@ __device__ __forceinline__ float ld_rep1(const void* base, uint64_t i) {
 template <int RDT, int RFIX, int SUB>
 __device__ __forceinline__ void sum_reps4(const RepPtrs& reps, int nrep, const uint64_t (&idx)[SUB],
                                           f32x4 (&acc)[SUB]) {
+  constexpr int B = ZERO_REP_BATCH;   // replica loads in flight per lane before their adds
   const int R = RFIX ? RFIX : nrep;
 #pragma unroll
   for (int u = 0; u < SUB; ++u) acc[u] = ld_rep4<RDT>(reps.p[0], idx[u]);
-  for (int k0 = 1; k0 < R; k0 += 8) {
-    f32x4 t[8][SUB];
+  for (int k0 = 1; k0 < R; k0 += B) {
+    f32x4 t[B][SUB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < B; ++j)
       if (k0 + j < R) {
 #pragma unroll
         for (int u = 0; u < SUB; ++u) t[j][u] = ld_rep4<RDT>(reps.p[k0 + j], idx[u]);
       }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < B; ++j)
       if (k0 + j < R) {
 #pragma unroll
         for (int u = 0; u < SUB; ++u) acc[u] = acc[u] + t[j][u];

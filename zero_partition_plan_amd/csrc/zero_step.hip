@@ -30,18 +30,10 @@
 #ifndef ZERO_REP_BATCH
 #define ZERO_REP_BATCH 8           // replica loads issued together before they are summed
 #endif
-#ifndef ZERO_ADAM_WAVES
-#define ZERO_ADAM_WAVES 0          // > 0: ask for at least this many waves per SIMD (register cap)
-#endif
-#if ZERO_ADAM_WAVES > 0
-#define ZERO_ADAM_WAVES_ATTR __attribute__((amdgpu_waves_per_eu(ZERO_ADAM_WAVES)))
-#else
-#define ZERO_ADAM_WAVES_ATTR
-#endif
 
 namespace {
 
-constexpr int kBlock = 256;            // reduce / squared-norm kernels
+constexpr int kBlock = 256;            // the per-element tail kernels and the squared-norm finish
 constexpr int kWaves = kBlock / 64;
 constexpr int kAdamBlock = ZERO_ADAM_BLOCK;
 
@@ -190,7 +182,7 @@ __device__ __forceinline__ void adam1(float acc, float& p, float& m, float& v, c
 // aligned) one element per thread.
 
 template <int RDT, int ODT, bool L2, int RFIX, bool SKIP>
-__global__ __launch_bounds__(kAdamBlock) ZERO_ADAM_WAVES_ATTR void k_adam_step(
+__global__ __launch_bounds__(kAdamBlock) void k_adam_step(
     RepPtrs reps, int nrep, uint64_t first_tile, StepScalars sc, float* __restrict__ P,
     float* __restrict__ M, float* __restrict__ V, void* __restrict__ out,
     const int32_t* __restrict__ skip) {
@@ -304,8 +296,7 @@ __device__ __forceinline__ void reduce_tile(const RepPtrs& reps, int nrep, uint6
     for (int u = 0; u < kRedSub; ++u) idx[u] = base + (uint64_t)u * 256 + threadIdx.x * 4u;
     f32x4 acc[kRedSub];
     sum_reps4<RDT, RFIX, kRedSub>(reps, nrep, idx, acc);
-#pragma unroll
-    for (int u = 0; u < kRedSub; ++u) {
+    unroll<kRedSub>([&](auto u) {
       if (G != nullptr) st(reinterpret_cast<f32x4*>(G + idx[u]), acc[u]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -313,7 +304,7 @@ __device__ __forceinline__ void reduce_tile(const RepPtrs& reps, int nrep, uint6
         const double d = (double)acc[u][q] * sq_scale;
         sq += d * d;
       }
-    }
+    });
   } else {
     for (int u = 0; u < kRedSub; ++u)
       for (int q = 0; q < 4; ++q) {

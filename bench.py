@@ -530,19 +530,19 @@ def pct(xs, q):
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(name: str, seconds: float):
-    """The oracle, as it stands, on windows of the same workload drawn on the host."""
+def _oracle_passes(name: str, seconds: float, seed_offset: int = 0):
+    """Run the oracle's step over one host-drawn window of the workload until `seconds` have gone."""
     import oracle as O
     from workloads import WORKLOADS
     from workloads import host as H
 
     w = WORKLOADS["llama13b" if name.startswith("llama13b") else name]
-    win = 1 << 21
+    win = CPU_WINDOW
     plan = O.partition_plan(w.n, w.nd)
     begin, _ = O.shard_range(plan, w.ranks[0])
     hp = O.AdamHParams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                        weight_decay=w.weight_decay, wd_mode=w.wd_mode, step=w.warm_steps + 1)
-    inp = H.rank_inputs(w, begin, win, win)
+    inp = H.rank_inputs(w, begin, win, win, seed_offset=seed_offset)
     elems, t_used = 0, 0.0
     while t_used < seconds:
         t0 = time.perf_counter()
@@ -550,11 +550,36 @@ def cpu_baseline(name: str, seconds: float):
                        w.out_dtypes[0])
         t_used += time.perf_counter() - t0
         elems += win
-    return {"value": elems / t_used, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"{elems // win} passes of the numpy oracle (replica sum + AdamW + cast) over a "
-                      f"{win}-element window of the {name} shard drawn on the host, "
-                      f"{t_used:.1f} s of one host core (numpy ufuncs are single-threaded); "
-                      f"host has {os.cpu_count()} logical CPUs"}
+    return elems, t_used
+
+
+def _oracle_worker(args):
+    return _oracle_passes(*args)
+
+
+CPU_WINDOW = 1 << 21
+CPU_WORKERS = 16            # the machine's host-core share for one GPU
+
+
+def cpu_baseline(name: str, seconds: float):
+    """The oracle, as it stands, on windows of the same workload drawn on the host: one process
+    (numpy ufuncs are single-threaded, so one core), then CPU_WORKERS processes side by side."""
+    import multiprocessing as mp
+
+    elems, t_used = _oracle_passes(name, seconds)
+    single = elems / t_used
+    workers = min(CPU_WORKERS, os.cpu_count() or 1)
+    with mp.get_context("spawn").Pool(workers) as pool:
+        res = pool.map(_oracle_worker, [(name, seconds * 2 / 3, k + 1) for k in range(workers)])
+    multi = sum(e / t for e, t in res)
+    return {"value": single, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{elems // CPU_WINDOW} passes of the numpy oracle (replica sum + AdamW + cast) "
+                      f"over a {CPU_WINDOW}-element window of the {name} shard drawn on the host, "
+                      f"{t_used:.1f} s of one host core; host has {os.cpu_count()} logical CPUs",
+            "all_cores": {"value": multi, "unit": "params/s", "cores": workers,
+                          "sample": f"{workers} processes, each the same oracle on its own "
+                                    f"{CPU_WINDOW}-element window for {seconds * 2 / 3:.0f} s; "
+                                    f"value = sum of their rates"}}
 
 
 # ----------------------------------------------------------------------------- main

@@ -5,10 +5,10 @@
  * each rank keeps only its shard of the Adam state (fp32 parameter copy, m, v: 12 bytes per
  * parameter), reduces the gradient for its shard only, updates its own parameters, and hands the
  * 16-bit result to an all-gather that rebuilds the full parameter buffer on every rank.
- * Sources, cited by page title and section:
- *   "ZeRO 优化器的三个阶段深度对比：显存节省与通信开销的量化分析" (wmrh.cn), sections 一 and 二;
- *   "ZeRO 优化器：把显存“分”着用" (5688vip.com), ZeRO Stage 1 and ZeRO Stage 2;
- *   "ZeRO Optimization（零冗余优化）" (ai-master.cc glossary), core-operations and stages lists.
+ * Sources, cited by page title and section (P1..P3 below):
+ *   P1 "ZeRO 优化器的三个阶段深度对比：显存节省与通信开销的量化分析" (wmrh.cn), sections 一 to 四;
+ *   P2 "ZeRO 优化器：把显存“分”着用" (5688vip.com), ZeRO Stage 1 to 3 and ZeRO-Offload;
+ *   P3 "ZeRO Optimization（零冗余优化）" (ai-master.cc glossary), core-operations and stages lists.
  * The pages print no update equations and say nothing about loss scaling, overflow or clipping;
  * the exact arithmetic below is this library's reading and is spelled out per entry point.
  *
@@ -18,7 +18,8 @@
  *   - Ownership: the caller allocates and frees every buffer. The library allocates no memory and
  *     keeps no state except a thread-local error message and a per-device launch-size cache.
  *   - Streams: device work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and
- *     never synchronised; device outputs are valid once the stream reaches that point.
+ *     never synchronised, except where an entry point says otherwise; device outputs are valid once
+ *     the stream reaches that point.
  *   - Errors: arguments are checked before any device work; on a bad argument nothing is launched
  *     and nothing is written. A failed launch returns ZERO_E_HIP. Details: zero_last_error().
  *   - n == 0 is valid and enqueues nothing (except where stated); arrays of length 0 may be NULL.
@@ -178,7 +179,7 @@ zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, 
  * Aliasing: master, m, v, out_param must not overlap each other or any replica.
  * Any alignment is accepted; 16-byte-aligned arrays take the vector path.
  * Errors: NULLs, bad source, bad hparams, aliasing -> ZERO_E_INVAL; out_dtype ZERO_F32 ->
- * ZERO_E_UNSUPPORTED; n*4 >= 2^64 -> ZERO_E_OVERFLOW. */
+ * ZERO_E_UNSUPPORTED; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
 zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float grad_scale,
                                  float* master, float* m, float* v, const zero_adam_hparams* hp,
                                  void* out_param, int32_t out_dtype, const int32_t* d_skip,
@@ -229,9 +230,10 @@ typedef struct {
  * fp16). Chunks are double-buffered: the GPU reduces and copies chunk c+1 while the host updates
  * chunk c, and chunk c's parameters travel back on h2d_stream while the host works on the next.
  * Results equal zero_adam_shard_step's bit for bit. Host-synchronous: returns once every parameter
- * copy has landed; it creates and destroys four HIP events per call. Errors: as
- * zero_host_adam_step and zero_reduce_shard, plus NULL or incomplete buffers -> ZERO_E_INVAL and
- * HIP failures -> ZERO_E_HIP (the state may then be partly updated). */
+ * copy has landed; it creates and destroys four HIP events per call. Aliasing: d_out_param, the
+ * staging d_grad and the replicas must not overlap. Errors: as zero_host_adam_step and
+ * zero_reduce_shard, plus NULL or incomplete buffers or device aliasing -> ZERO_E_INVAL and HIP
+ * failures -> ZERO_E_HIP (the state may then be partly updated). */
 zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_scale,
                               float* h_master, float* h_m, float* h_v, const zero_adam_hparams* hp,
                               void* d_out_param, int32_t out_dtype,

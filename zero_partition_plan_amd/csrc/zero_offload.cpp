@@ -197,6 +197,14 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
   const int rb = (int)zero::dtype_bytes(src->dtype);
   if (!src->ptrs || src->count == 0 || src->count > ZERO_MAX_REPLICAS)
     return zero::fail(ZERO_E_INVAL, "%s: bad gradient source", fn);
+  if (zero::overlaps(d_out_param, n * 2, buf->d_grad, 2 * C * 4))
+    return zero::fail(ZERO_E_INVAL, "%s: the slot overlaps the gradient staging", fn);
+  for (uint32_t r = 0; r < src->count; ++r) {
+    if (zero::overlaps(d_out_param, n * 2, src->ptrs[r], n * rb))
+      return zero::fail(ZERO_E_INVAL, "%s: the slot overlaps replica %u", fn, r);
+    if (zero::overlaps(buf->d_grad, 2 * C * 4, src->ptrs[r], n * rb))
+      return zero::fail(ZERO_E_INVAL, "%s: the gradient staging overlaps replica %u", fn, r);
+  }
 
   hipStream_t main = static_cast<hipStream_t>(stream);
   hipStream_t back = buf->h2d_stream ? static_cast<hipStream_t>(buf->h2d_stream) : main;

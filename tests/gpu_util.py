@@ -3,6 +3,8 @@
 import numpy as np
 import torch
 
+from bitcmp import assert_bits_equal, assert_bits_equal_nan, is_nan_bits  # noqa: F401 (re-exported)
+
 DEV = "cuda:0"
 _T16 = {"bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -34,12 +36,6 @@ def empty16(n: int, dtype: str, fill: float = 0.0) -> torch.Tensor:
     return torch.full((n,), fill, dtype=_T16[dtype], device=DEV)
 
 
-def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str):
-    if not np.array_equal(got, want):
-        bad = np.nonzero(got != want)[0]
-        raise AssertionError(f"{what}: {bad.size} of {want.size} differ; first at {bad[:5].tolist()}: "
-                             f"got {[hex(int(x)) for x in got[bad[:5]]]} want {[hex(int(x)) for x in want[bad[:5]]]}")
-
-
 def banner(msg: str):
     print(f"[gpu] {msg}", flush=True)
+

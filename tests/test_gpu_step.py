@@ -11,10 +11,11 @@ import torch
 
 import oracle as O
 import zero_partition_plan_amd as Z
-from gpu_util import (DEV, assert_bits_equal, banner, bits16, bits32, dev_f32, dev_rep, empty16,
-                      f32_bits)
+from gpu_util import (DEV, assert_bits_equal, assert_bits_equal_nan, banner, bits16, bits32, dev_f32,
+                      dev_rep, empty16, f32_bits)
 from workloads import WORKLOADS
 from workloads import host as H
+from workloads.extremes import EXTREME_CASES, f16_all_patterns, f32_patterns, mixed_state
 
 pytestmark = pytest.mark.gpu
 
@@ -364,3 +365,78 @@ def test_two_pass_clip_and_overflow_skip(inject):
     assert_bits_equal(m, f32_bits(m2), "m")
     assert_bits_equal(v, f32_bits(v2), "v")
     assert_bits_equal(o, o2, "fp16 params")
+
+
+# --- IEEE special cases inside the update: subnormals, overflow, 0/0, inf/inf, signed zeros ----------
+
+
+@pytest.mark.parametrize("case", range(len(EXTREME_CASES)))
+@pytest.mark.parametrize("rep", ["f32", "bf16"])
+def test_step_ieee_special_cases(case, rep):
+    """Operands drawn over the whole binary32 range, so that subnormal inputs and results, overflow,
+    0/0 and inf/inf arise inside the update. Every non-NaN fp32 and 16-bit result equals the oracle's
+    bit for bit; NaN results must be NaN on both sides."""
+    regimes, gs, hpx = EXTREME_CASES[case]
+    n = 5 * TILE + 77
+    rng = np.random.default_rng(700 + case)
+    g, p, m, v = mixed_state(rng, n, regimes)
+    if rep == "f32":
+        reps = g[None, :].copy()
+    else:   # three bf16 replicas whose exact fp32 sum spans the same range
+        third = (g.view(np.uint32) & 0xFFFF0000).view(np.float32)
+        reps = np.stack([(third.view(np.uint32) >> 16).astype(np.uint16)] * 3)
+    hp_kw = {**HP, **hpx}
+    banner(f"ieee special cases {case} {rep} {regimes} gs={gs}")
+    for out_dtype in ("bf16", "f16"):
+        got = _run_step(reps, rep, n, p, m, v, hp_kw, out_dtype, grad_scale=gs)
+        with np.errstate(all="ignore"):
+            want = O.sharded_step(list(reps), rep, gs, p, m, v, O.AdamHParams(**hp_kw), out_dtype)
+        for k, what in enumerate(("master", "m", "v")):
+            assert_bits_equal_nan(got[k], f32_bits(want[k]), f"{what} ({out_dtype})")
+        assert_bits_equal_nan(got[3], want[3], f"out {out_dtype}", out_dtype)
+
+
+@pytest.mark.parametrize("gs", [1.0, 2.0 ** -16])
+def test_step_every_fp16_gradient_pattern(gs):
+    """One fp16 replica holding every binary16 pattern (subnormals, infinities, NaNs), widened
+    exactly and pushed through the update from warm state."""
+    h = f16_all_patterns()
+    n = h.size
+    rng = np.random.default_rng(77)
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (rng.random(n) * 1e-7).astype(np.float32)
+    banner(f"every fp16 gradient pattern gs={gs}")
+    got = _run_step(h[None, :], "f16", n, p, m, v, HP, "bf16", grad_scale=gs)
+    with np.errstate(all="ignore"):
+        want = O.sharded_step([h], "f16", gs, p, m, v, O.AdamHParams(**HP), "bf16")
+    for k, what in enumerate(("master", "m", "v")):
+        assert_bits_equal_nan(got[k], f32_bits(want[k]), what)
+    assert_bits_equal_nan(got[3], want[3], "out", "bf16")
+
+
+def test_reduce_and_sqnorm_over_the_full_range():
+    """The reduce pass over finite operands spanning every binade: the fp32 sum bit for bit and
+    the fp64 squared norm against an exact sum of the same squares."""
+    n = 7 * TILE + 301
+    rng = np.random.default_rng(91)
+    reps = np.stack([f32_patterns(rng, n, "full") * np.float32(2.0 ** -2) for _ in range(3)])
+    banner("reduce over the full fp32 range")
+    d_r = [dev_f32(r) for r in reps]
+    d_g = torch.empty(n, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    parts = torch.empty(Z.zero_sq_partials_len(n), dtype=torch.float64, device=DEV)
+    sq = torch.empty(1, dtype=torch.float64, device=DEV)
+    Z.zero_reduce_shard(d_r, n, d_g, nonfinite=flag, sq_partials=parts, sq_scale=2.0 ** -16)
+    Z.zero_shard_sqnorm(None, n, 2.0 ** -16, parts, sq)
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        acc = O.replica_sum(list(reps), "f32")
+    assert_bits_equal(bits32(d_g), f32_bits(acc), "reduced gradient")
+    assert int(flag.item()) == int(O.nonfinite_flag(acc))
+    finite = np.isfinite(acc)
+    if finite.all():
+        want = O.shard_sqnorm(acc, 2.0 ** -16)
+        assert abs(sq.item() - want) <= 1e-10 * want
+    else:
+        assert math.isinf(sq.item()) or math.isnan(sq.item())

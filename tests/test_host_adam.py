@@ -6,6 +6,8 @@ import pytest
 
 import oracle as O
 import zero_partition_plan_amd as Z
+from bitcmp import assert_bits_equal_nan
+from workloads.extremes import EXTREME_CASES, mixed_state
 
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 
@@ -114,3 +116,25 @@ def test_host_step_errors():
                               out_dtype=Z.ZERO_F32)
     assert e.value.status == 3
     Z.zero_host_adam_step(None, 0, 1.0, None, None, None, Z.adam_hparams())              # n = 0 no-op
+
+
+@pytest.mark.parametrize("case", range(len(EXTREME_CASES)))
+@pytest.mark.parametrize("threads", [1, 4])
+def test_host_step_ieee_special_cases(case, threads):
+    """Operands over the whole binary32 range (subnormals, overflow, 0/0, inf/inf, signed zeros):
+    every non-NaN result equals the oracle's bit for bit, and NaN results are NaN on both sides
+    (operand order inside a vector loop may pick a different NaN's payload)."""
+    regimes, gs, hpx = EXTREME_CASES[case]
+    n = 70_001
+    rng = np.random.default_rng(900 + case)
+    g, p, m, v = mixed_state(rng, n, regimes)
+    hp = {**HP, "step": 3, **hpx}
+    for odt in ("bf16", "f16"):
+        p2, m2, v2, out = p.copy(), m.copy(), v.copy(), np.zeros(n, np.uint16)
+        Z.zero_host_adam_step(g, n, gs, p2, m2, v2, Z.adam_hparams(**hp), out=out,
+                              out_dtype={"bf16": Z.ZERO_BF16, "f16": Z.ZERO_F16}[odt], threads=threads)
+        with np.errstate(all="ignore"):
+            wp, wm, wv, wo = O.sharded_step([g], "f32", gs, p, m, v, O.AdamHParams(**hp), odt)
+        for got, want, what in ((p2, wp, "master"), (m2, wm, "m"), (v2, wv, "v")):
+            assert_bits_equal_nan(got.view(np.uint32), want.view(np.uint32), f"{what} ({odt})")
+        assert_bits_equal_nan(out, wo, f"out {odt}", odt)

@@ -5,7 +5,8 @@ Default workload: the Llama-7B-shaped flat parameter space (6,738,415,616 elemen
 ranks, one rank's 842,301,952-element shard: 8 bf16 gradient replicas summed in fixed order,
 AdamW on the fp32 master / m / v (warm state, t = 11), bf16 cast into the rank's slot of the full
 gathered parameter buffer. One step = one fused kernel launch. Inputs are drawn on the device and
-are resident in HBM before the timed region.
+are resident in HBM before the timed region, all arrays of the step in one arena laid out by
+zero_arena_layout (arrays a kernel walks together start at staggered offsets past 256 MiB lines).
 
 Prints one JSON line (see the fields below). Flags:
   --gpus N         only 1 is supported: this path runs on one GPU's shard
@@ -14,6 +15,8 @@ Prints one JSON line (see the fields below). Flags:
   --workload NAME  llama7b (default), gpt2, llama13b (two-pass clip path), gpt3 (64 Mi windows),
                    gather7b (ZeRO-3: every Llama-7B layer gathered from its 8 rank shards),
                    offload7b (ZeRO-Offload: the 7B shard's Adam state in host memory)
+  --placement P    arena (default) or separate: every array of the step in its own allocation
+  --no-context     skip the context legs (copy ceiling, separate-placement step, cold launches)
   --cpu-seconds S  budget of the oracle's CPU baseline (default 12; 0 skips it)
   --copy-calib MB  also run a plain device copy of MB MiB 5 times (for counter calibration)
   --summarize      (no GPU) turn the rocprofv3 CSVs of the profile commands into the summaries
@@ -152,7 +155,7 @@ def profile_dirs(workload: str) -> dict:
 
 def profile_commands(workload: str) -> dict:
     d = profile_dirs(workload)
-    run = f"python -u bench.py --workload {workload}"
+    run = f"python -u bench.py --workload {workload} --no-context"
     return {
         "trace": f"rocprofv3 --kernel-trace --stats -T -d {d['trace']} -o kt -f csv -- "
                  f"{run} --steps 10 --warmup 2 --cpu-seconds 0",
@@ -273,32 +276,44 @@ def summarize(workload: str):
 
 # ----------------------------------------------------------------------------- workloads
 
-def setup(name: str):
+def setup(name: str, placement: str = "arena"):
+    """Inputs of one rank's step, drawn on the device. With ``placement`` "arena" every array of the
+    step lives in one allocation laid out by zero_arena_layout; "separate" gives each its own."""
     import torch
 
     import zero_partition_plan_amd as Z
     from workloads import WORKLOADS
     from workloads import device as D
+    from workloads.placement import step_arrays
 
     w = WORKLOADS["llama13b"] if name.startswith("llama13b") else WORKLOADS[name]
     if name == "llama13b-clean":
         w = dataclasses.replace(w, inf_rate=0.0)
+    two_pass = name.startswith("llama13b")
     plan = Z.zero_partition_plan(w.n, w.nd)
     rank = w.ranks[0]
     begin, valid = Z.zero_shard_range(plan, rank)
     S = plan.shard_elems
     dev = torch.device("cuda:0")
-    log(f"workload {name}: N={w.n} Nd={w.nd} rank={rank} S={S} R={w.reps}x{w.rep_dtype}")
-    inp = D.rank_inputs(w, begin, S, valid, device=dev, rep_size=w.window)
+    log(f"workload {name}: N={w.n} Nd={w.nd} rank={rank} S={S} R={w.reps}x{w.rep_dtype} "
+        f"placement={placement}")
+    storage, views = None, None
+    if placement == "arena":
+        storage, views = Z.arena(step_arrays(w, S, begin, plan.padded_n, two_pass), device=dev)
+        log(f"arena: {storage.numel() / 2**30:.2f} GiB for {len(views)} arrays")
+    empty = (lambda nm, n, dt: views[nm]) if views else None
+    inp = D.rank_inputs(w, begin, S, valid, device=dev, rep_size=w.window, empty=empty)
     out_t = torch.float16 if w.out_dtypes[0] == "f16" else torch.bfloat16
-    state = dict(w=w, plan=plan, S=S, begin=begin, inp=inp, t=w.warm_steps + 1)
-    if w.window is None and not name.startswith("llama13b"):
-        state["full"] = torch.zeros(plan.padded_n, dtype=out_t, device=dev)
+    state = dict(w=w, plan=plan, S=S, begin=begin, inp=inp, t=w.warm_steps + 1, arena=storage,
+                 placement=placement)
+    if w.window is None and not two_pass:
+        state["full"] = (views["full"].zero_() if views else
+                         torch.zeros(plan.padded_n, dtype=out_t, device=dev))
         state["slot"] = state["full"][begin:begin + S]
     else:
-        state["slot"] = torch.zeros(S, dtype=out_t, device=dev)
-    if name.startswith("llama13b"):
-        state["g"] = torch.empty(S, device=dev)
+        state["slot"] = views["slot"].zero_() if views else torch.zeros(S, dtype=out_t, device=dev)
+    if two_pass:
+        state["g"] = views["g"] if views else torch.empty(S, device=dev)
         state["flag"] = torch.zeros(1, dtype=torch.int32, device=dev)
         state["host_sq"] = torch.zeros(1, dtype=torch.float64, pin_memory=True)
         state["host_flag"] = torch.zeros(1, dtype=torch.int32, pin_memory=True)
@@ -307,6 +322,27 @@ def setup(name: str):
         state["sq"] = torch.empty(1, dtype=torch.float64, device=dev)
     torch.cuda.synchronize()
     return state
+
+
+def placement_context(name: str, steps: int = 5):
+    """The same step with every array in its own allocation (the default allocator's placement)."""
+    import torch
+    st = setup(name, "separate")
+    step = step_two_pass if name.startswith("llama13b") else step_fused
+    for _ in range(2):
+        step(st, Spans(False))
+    torch.cuda.synchronize()
+    e0, e1 = new_event(True), new_event()
+    for _ in range(steps):
+        step(st, Spans(False))
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del st
+    torch.cuda.empty_cache()
+    return {"separate_ms_per_step": ms, "steps": steps,
+            "note": "the same step with master, m, v, every replica row and the output each in its own "
+                    "allocation; the timed line above places them in one arena (zero_arena_layout)"}
 
 
 def setup_gather():
@@ -592,6 +628,12 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "gpt2", "llama13b", "llama13b-clean", "gpt3", "gather7b",
                              "offload7b"])
+    ap.add_argument("--placement", default="arena", choices=["arena", "separate"],
+                    help="arrays of the step in one arena laid out by zero_arena_layout, or each in "
+                         "its own allocation")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context legs (copy ceiling, separate-placement step, cold launches), "
+                         "so that a profiler sees only the timed step's launches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calib", type=int, default=0)
     ap.add_argument("--summarize", action="store_true")
@@ -624,7 +666,7 @@ def main(argv=None):
     elif args.workload == "offload7b":
         st, step = setup_offload(), step_offload
     else:
-        st = setup(args.workload)
+        st = setup(args.workload, args.placement)
         step = step_two_pass if args.workload.startswith("llama13b") else step_fused
     w, S = st["w"], st["S"]
 
@@ -685,7 +727,7 @@ def main(argv=None):
     traffic = recorded_traffic(args.workload, dom)
 
     cold = None
-    if args.workload == "gpt2":
+    if args.workload == "gpt2" and not args.no_context:
         cms = cold_launches(st)
         cold = {"median_ms": pct(cms, 0.5), "min_ms": min(cms), "p90_ms": pct(cms, 0.9),
                 "gbs_at_median": bpe[dom] * n_launch / pct(cms, 0.5) / 1e6,
@@ -693,9 +735,12 @@ def main(argv=None):
                         "roofline figures above are warm (back-to-back launches)"}
         log(f"cold launches: median {cold['median_ms']:.4f} ms -> {cold['gbs_at_median']:.0f} GB/s")
     context = None
-    if args.workload == "llama7b":
+    if args.workload == "llama7b" and not args.no_context:
         context = {"copy_ceiling": copy_ceiling()}
         log(f"copy ceiling: {context['copy_ceiling']['gbs']:.0f} GB/s")
+        if args.placement == "arena":
+            context["placement"] = placement_context(args.workload)
+            log(f"separate allocations: {context['placement']['separate_ms_per_step']:.4f} ms per step")
 
     if args.copy_calib:
         nb = args.copy_calib << 20
@@ -741,6 +786,7 @@ def main(argv=None):
             "replica_dtype": w.rep_dtype,
             "param_out_dtype": w.out_dtypes[0],
             "optimizer": f"AdamW wd={w.weight_decay}",
+            "placement": st.get("placement"),
             "first_timed_t": w.warm_steps + 1 + args.warmup,
             "launches_per_step": ({"k_reduce": -(-S // OFFLOAD_CHUNK)} if args.workload == "offload7b"
                                   else {k: v["launches"] / args.steps for k, v in per_kernel.items()}),

@@ -125,6 +125,36 @@ typedef struct {
 zero_status zero_choose_stage(const zero_plan* p, uint64_t usable_bytes, uint32_t param_b,
                               uint32_t grad_b, uint32_t opt_b, zero_stage_choice* out);
 
+/* Placement of the arrays of one pass in a single device allocation (the "arena"), so that arrays
+ * walked at the same element index do not start at addresses the memory interleave maps alike.
+ * Not an operation of the pages: it places the rank's shard arrays (P1 section 二: each rank keeps
+ * its own shard of parameters, gradients and optimizer state) for bandwidth on this GPU.
+ * arrays[i]: bytes (the array's size), hot_offset (byte offset inside the array where the kernel's
+ * walk starts, e.g. r*S*2 for rank r's slot inside a gathered 16-bit buffer; else 0), group (arrays
+ * a kernel reads or writes at the same element index share a group id; ids are arbitrary) and
+ * elem_bytes (2 or 4). Arrays are placed in the given order, each after the previous one ends; the
+ * k-th member of a group (counted in that order) gets its hot start at a multiple of
+ * ZERO_ARENA_GRANULE plus k * ZERO_ARENA_STAGGER16 (16-bit) or k * ZERO_ARENA_STAGGER32 (fp32).
+ * offsets[i] (host, count entries) receives array i's byte offset from the arena start and
+ * *total_bytes the size to allocate. Only offsets relative to one allocation matter: any
+ * 256-byte-aligned allocation of total_bytes works, and every hot start is then 2 KiB aligned.
+ * Host only. Errors: NULL, count 0 or > ZERO_ARENA_MAX_ARRAYS, elem_bytes not 2 or 4, hot_offset or
+ * bytes not whole elements or hot_offset > bytes -> ZERO_E_INVAL; a total >= 2^64 ->
+ * ZERO_E_OVERFLOW. */
+#define ZERO_ARENA_MAX_ARRAYS 256
+#define ZERO_ARENA_GRANULE (256ull << 20)
+#define ZERO_ARENA_STAGGER16 2048ull
+#define ZERO_ARENA_STAGGER32 12288ull
+typedef struct {
+  uint64_t bytes;
+  uint64_t hot_offset;
+  uint32_t group;
+  uint32_t elem_bytes;
+} zero_arena_array;
+
+zero_status zero_arena_layout(const zero_arena_array* arrays, uint32_t count, uint64_t* offsets,
+                              uint64_t* total_bytes);
+
 /* The fp32 constants of step hp->step, each formed in fp64 and rounded once:
  * b1 = f32(beta1), b2 = f32(beta2), c1 = f32(1-beta1), c2 = f32(1-beta2),
  * ss = f32(lr / (1 - pow(beta1, t))), bc = f32(sqrt(1 - pow(beta2, t))), e = f32(eps),

@@ -1,7 +1,7 @@
 // Drives every host-only entry point of the library under AddressSanitizer and UBSan: the
-// partition plan, shard ranges, per-stage bytes, the stage choice, the Adam constants and the host
-// update (all sizes from 0 up, unaligned arrays, every thread count, both 16-bit outputs, the
-// error paths). Built with a plain host compiler from the sources that make no HIP calls.
+// partition plan, shard ranges, per-stage bytes, the stage choice, the arena layout, the Adam
+// constants and the host update (all sizes from 0 up, unaligned arrays, every thread count, both
+// 16-bit outputs, the error paths). Built with a plain host compiler from the sources that make no HIP calls.
 // Exits non-zero on a wrong status or a result that differs between thread counts.
 #include <stdio.h>
 #include <stdlib.h>
@@ -135,8 +135,43 @@ static void host_updates() {
          ZERO_E_OVERFLOW);
 }
 
+static void arenas() {
+  uint64_t seed = 7;
+  for (int trial = 0; trial < 200; ++trial) {
+    const uint32_t count = 1 + lcg(&seed) % ZERO_ARENA_MAX_ARRAYS;
+    std::vector<zero_arena_array> a(count);
+    for (auto& x : a) {
+      x.elem_bytes = (lcg(&seed) & 1) ? 4 : 2;
+      const uint64_t n = lcg(&seed) % (1u << (lcg(&seed) % 31));
+      x.bytes = n * x.elem_bytes;
+      x.hot_offset = n ? (lcg(&seed) % (n + 1)) * x.elem_bytes : 0;
+      x.group = lcg(&seed) % 5;
+    }
+    std::vector<uint64_t> off(count);
+    uint64_t total = 0;
+    EXPECT(zero_arena_layout(a.data(), count, off.data(), &total) == ZERO_OK);
+    uint64_t end = 0;
+    for (uint32_t i = 0; i < count; ++i) {
+      EXPECT(off[i] >= end && off[i] - end < ZERO_ARENA_GRANULE);
+      EXPECT((off[i] + a[i].hot_offset) % 2048 == 0);
+      end = off[i] + a[i].bytes;
+    }
+    EXPECT(total == end);
+  }
+  zero_arena_array big[2] = {{1ull << 63, 0, 0, 2}, {1ull << 63, 0, 1, 2}};
+  uint64_t off[ZERO_ARENA_MAX_ARRAYS + 1], total;
+  EXPECT(zero_arena_layout(big, 2, off, &total) == ZERO_E_OVERFLOW);
+  zero_arena_array bad = {1024, 0, 0, 3};
+  EXPECT(zero_arena_layout(&bad, 1, off, &total) == ZERO_E_INVAL);
+  EXPECT(zero_arena_layout(big, 0, off, &total) == ZERO_E_INVAL);
+  EXPECT(zero_arena_layout(NULL, 1, off, &total) == ZERO_E_INVAL);
+  std::vector<zero_arena_array> many(ZERO_ARENA_MAX_ARRAYS + 1, zero_arena_array{64, 0, 0, 2});
+  EXPECT(zero_arena_layout(many.data(), ZERO_ARENA_MAX_ARRAYS + 1, off, &total) == ZERO_E_INVAL);
+}
+
 int main() {
   plans();
+  arenas();
   derive();
   host_updates();
   if (failures) {

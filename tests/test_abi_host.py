@@ -202,3 +202,94 @@ def test_status_strings():
     for s in range(5):
         assert Z.zero_status_str(s)
     assert Z.zero_status_str(99) == "unknown status"
+
+
+Q = 256 << 20                                   # ZERO_ARENA_GRANULE
+STAGGER = {2: 2048, 4: 12288}                   # ZERO_ARENA_STAGGER16 / 32
+
+
+def test_arena_constants_match_header():
+    text = open(HEADER).read()
+    assert re.search(r"#define ZERO_ARENA_GRANULE \(256ull << 20\)", text)
+    assert int(re.search(r"#define ZERO_ARENA_STAGGER16 (\d+)ull", text).group(1)) == STAGGER[2]
+    assert int(re.search(r"#define ZERO_ARENA_STAGGER32 (\d+)ull", text).group(1)) == STAGGER[4]
+    assert ctypes.sizeof(Z.ZeroArenaArray) == 24
+
+
+def _check_layout(arrays, offs, total):
+    member, end = {}, 0
+    for (nbytes, hot, group, eb), off in zip(arrays, offs):
+        k = member.get(group, 0)
+        member[group] = k + 1
+        assert off >= end and off - end < Q                  # in order, no overlap, gap < granule
+        assert (off + hot) % Q == (k * STAGGER[eb]) % Q      # hot start: granule + k * stagger
+        assert off % eb == 0 and (off + hot) % 2048 == 0
+        end = off + nbytes
+    assert total == end
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_arena_layout_rule(seed):
+    rng = np.random.default_rng(seed)
+    arrays = []
+    for _ in range(int(rng.integers(1, 40))):
+        eb = int(rng.choice([2, 4]))
+        n = int(rng.integers(0, 1 << int(rng.integers(1, 32))))
+        hot = int(rng.integers(0, n + 1)) if n and rng.random() < 0.3 else 0
+        arrays.append((n * eb, hot * eb, int(rng.integers(0, 4)) * 977, eb))
+    offs, total = Z.zero_arena_layout(arrays)
+    _check_layout(arrays, offs, total)
+
+
+def test_arena_layout_of_the_7b_step():
+    """Eight bf16 replica rows and the gathered buffer (walked from rank 0's slot) in one group,
+    master/m/v in another: hot starts at 0, 2, .., 16 KiB and 0, 12, 24 KiB past 256 MiB lines."""
+    S, P = 842_301_952, 6_738_415_616
+    arrays = [(2 * S, 0, 0, 2)] * 8 + [(2 * P, 0, 0, 2)] + [(4 * S, 0, 1, 4)] * 3
+    offs, total = Z.zero_arena_layout(arrays)
+    _check_layout(arrays, offs, total)
+    assert [(o % Q) for o in offs] == [2048 * k for k in range(9)] + [0, 12288, 24576]
+    assert total < 2 * P + 11 * 4 * S
+
+
+def test_arena_layout_errors():
+    ok = (1024, 0, 0, 2)
+    for bad in [(1024, 0, 0, 3), (1024, 2048, 0, 2), (1023, 0, 0, 2), (1024, 2, 0, 4)]:
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_arena_layout([ok, bad])
+        assert e.value.status == 1, bad
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_arena_layout([])
+    assert e.value.status == 1
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_arena_layout([ok] * 257)
+    assert e.value.status == 1
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_arena_layout([(1 << 63, 0, 0, 2), (1 << 63, 0, 1, 2)])
+    assert e.value.status == 2
+    L = Z.lib()
+    arr = (Z.ZeroArenaArray * 1)(Z.ZeroArenaArray(64, 0, 0, 2))
+    out = (ctypes.c_uint64 * 1)()
+    tot = ctypes.c_uint64()
+    assert L.zero_arena_layout(None, 1, out, ctypes.byref(tot)) == 1
+    assert L.zero_arena_layout(arr, 1, None, ctypes.byref(tot)) == 1
+    assert L.zero_arena_layout(arr, 1, out, None) == 1
+
+
+def test_arena_views_on_host_memory():
+    import torch
+    specs = [("a", 1000, torch.bfloat16, 0, 0), ("b", 3000, torch.float16, 0, 17),
+             ("c", 513, torch.float32, 1, 0), ("d", 7, torch.float32, 1, 0)]
+    storage, views = Z.arena(specs, device="cpu")
+    base = storage.data_ptr()
+    offs, total = Z.zero_arena_layout([(n * t.element_size(), h * t.element_size(), g, t.element_size())
+                                       for (_, n, t, g, h) in [(s[0], s[1], torch.empty(0, dtype=s[2]),
+                                                                s[3], s[4]) for s in specs]])
+    assert storage.numel() == total
+    for (name, n, dt, _, _), off in zip(specs, offs):
+        v = views[name]
+        assert v.dtype == dt and v.shape == (n,) and v.data_ptr() - base == off
+    for i, (name, *_rest) in enumerate(specs):  # the views do not overlap
+        views[name].fill_(float(i + 1))
+    for i, (name, *_rest) in enumerate(specs):
+        assert (views[name] == float(i + 1)).all(), name

@@ -2,7 +2,9 @@
 
 Inputs are drawn on the device (seeded); windows of them are downloaded before the step, the
 step runs on the whole shard, and the same windows of the outputs are compared with the oracle
-run on the downloaded inputs: bit for bit for fp32 state and 16-bit parameters. For the squared
+run on the downloaded inputs: bit for bit for fp32 state and 16-bit parameters. The 7B, 13B and
+GPT-3 shards sit in one arena placed by zero_arena_layout, as the benchmark places them; the GPT-2
+shard uses separate allocations. For the squared
 norm, sampled tiles' fp64 partial sums (one per 512-element tile) are recomputed by the oracle from
 downloaded replica tiles, and the total is checked against the partials."""
 
@@ -19,6 +21,7 @@ from gpu_util import DEV, assert_bits_equal, banner, bits16, bits32, f32_bits
 from workloads import WORKLOADS
 from workloads import device as D
 from workloads import host as H
+from workloads.placement import step_arrays
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +60,20 @@ def _check_windows(w, wins, before, reps_win, d_p, d_m, d_v, d_out, hp, grad_sca
         assert_bits_equal(bits32(d_m[a:b]), f32_bits(m2), f"m [{a},{b})")
         assert_bits_equal(bits32(d_v[a:b]), f32_bits(v2), f"v [{a},{b})")
         assert_bits_equal(bits16(d_out[a:b]), o2, f"params [{a},{b})")
+
+
+def _placed(w, plan, begin, valid, two_pass=False):
+    """The rank's inputs drawn into one arena laid out as the benchmark lays it out."""
+    S = plan.shard_elems
+    storage, views = Z.arena(step_arrays(w, S, begin, plan.padded_n, two_pass), device=DEV)
+    inp = D.rank_inputs(w, begin, S, valid, device=DEV, rep_size=w.window,
+                        empty=lambda nm, n, dt: views[nm])
+    return storage, views, inp
+
+
+def _rows(reps, a, b):
+    """[R, b - a] copy of elements [a, b) of every replica row (a list of rows or one 2-D tensor)."""
+    return torch.stack([r[a:b] for r in reps])
 
 
 def _bits_to_np(t, dtype):
@@ -103,8 +120,8 @@ def test_llama7b_shard_full_size():
     begin, valid = Z.zero_shard_range(plan, r)
     S = plan.shard_elems
     banner(f"llama7b rank {r}: S={S}")
-    inp = D.rank_inputs(w, begin, S, valid, device=DEV)
-    d_full = torch.zeros(plan.padded_n, dtype=torch.bfloat16, device=DEV)
+    storage, views, inp = _placed(w, plan, begin, valid)
+    d_full = views["full"].zero_()
     wins = _windows(S)
     before = {ab: tuple(bits32(inp[k][ab[0]:ab[1]]).view(np.float32) for k in ("master", "m", "v"))
               for ab in wins}
@@ -112,11 +129,11 @@ def test_llama7b_shard_full_size():
     Z.zero_adam_shard_step(inp["reps"], S, 1.0, inp["master"], inp["m"], inp["v"],
                            Z.adam_hparams(**hp), out=d_full[begin:begin + S])
     torch.cuda.synchronize()
-    reps_win = lambda a, b: _bits_to_np(inp["reps"][:, a:b].contiguous(), "bf16")
+    reps_win = lambda a, b: _bits_to_np(_rows(inp["reps"], a, b), "bf16")
     _check_windows(w, wins, before, reps_win, inp["master"], inp["m"], inp["v"],
                    d_full[begin:begin + S], hp, 1.0, "bf16")
     assert torch.isfinite(inp["master"]).all()
-    del inp, d_full
+    del inp, d_full, views, storage
     _free()
 
 
@@ -132,9 +149,9 @@ def test_llama13b_two_pass_full_size(inject):
     begin, valid = Z.zero_shard_range(plan, r)
     S = plan.shard_elems
     banner(f"llama13b rank {r}: S={S} inject={inject}")
-    inp = D.rank_inputs(w, begin, S, valid, device=DEV)
-    d_slot = torch.zeros(S, dtype=torch.float16, device=DEV)
-    d_g = torch.empty(S, device=DEV)
+    storage, views, inp = _placed(w, plan, begin, valid, two_pass=True)
+    d_slot = views["slot"].zero_()
+    d_g = views["g"]
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
     parts = torch.empty(Z.zero_sq_partials_len(S), dtype=torch.float64, device=DEV)
     sq = torch.empty(1, dtype=torch.float64, device=DEV)
@@ -155,7 +172,7 @@ def test_llama13b_two_pass_full_size(inject):
     # the reduced gradient and the flag, on windows
     any_bad = False
     for (a, b) in wins:
-        reps = _bits_to_np(inp["reps"][:, a:b].contiguous(), "f16")
+        reps = _bits_to_np(_rows(inp["reps"], a, b), "f16")
         acc = O.replica_sum(list(reps), "f16")
         assert_bits_equal(bits32(d_g[a:b]), f32_bits(acc), f"reduced grad [{a},{b})")
         any_bad |= O.nonfinite_flag(acc)
@@ -166,7 +183,7 @@ def test_llama13b_two_pass_full_size(inject):
     ntiles = math.ceil(S / TILE)
     for t in (0, 1, ntiles // 2, ntiles - 1):
         acc = O.replica_sum(list(_bits_to_np(
-            inp["reps"][:, t * TILE:min(S, (t + 1) * TILE)].contiguous(), "f16")), "f16")
+            _rows(inp["reps"], t * TILE, min(S, (t + 1) * TILE)), "f16")), "f16")
         want = O.shard_sqnorm(acc, inv_ls)
         if np.isfinite(want):
             assert parts_h[t] == pytest.approx(want, rel=1e-12, abs=0), t
@@ -183,14 +200,14 @@ def test_llama13b_two_pass_full_size(inject):
             assert_bits_equal(bits32(inp["m"][a:b]), f32_bits(m0), "skipped m")
             assert not d_slot[a:b].any()
             continue
-        reps = _bits_to_np(inp["reps"][:, a:b].contiguous(), "f16")
+        reps = _bits_to_np(_rows(inp["reps"], a, b), "f16")
         acc = O.replica_sum(list(reps), "f16")
         p2, m2, v2, o2 = O.sharded_step([acc], "f32", gs, p0, m0, v0, O.AdamHParams(**_hp(w, 1)), "f16")
         assert_bits_equal(bits32(inp["master"][a:b]), f32_bits(p2), f"master [{a},{b})")
         assert_bits_equal(bits32(inp["m"][a:b]), f32_bits(m2), f"m [{a},{b})")
         assert_bits_equal(bits32(inp["v"][a:b]), f32_bits(v2), f"v [{a},{b})")
         assert_bits_equal(bits16(d_slot[a:b]), o2, f"fp16 params [{a},{b})")
-    del inp, d_g, d_slot
+    del inp, d_g, d_slot, views, storage
     _free()
 
 
@@ -203,8 +220,8 @@ def test_gpt3_windowed_shard_full_size():
     begin, valid = Z.zero_shard_range(plan, r)
     S, W = plan.shard_elems, w.window
     banner(f"gpt3 rank {r}: S={S} window={W}")
-    inp = D.rank_inputs(w, begin, S, valid, device=DEV, rep_size=W)
-    d_slot = torch.zeros(S, dtype=torch.bfloat16, device=DEV)
+    storage, views, inp = _placed(w, plan, begin, valid)
+    d_slot = views["slot"].zero_()
     last = (S // W) * W
     wins = [(0, WIN), (17 * W + 5, 17 * W + 5 + WIN), (last + 11, last + 11 + WIN), (S - WIN, S)]
     before = {ab: tuple(bits32(inp[k][ab[0]:ab[1]]).view(np.float32) for k in ("master", "m", "v"))
@@ -216,8 +233,8 @@ def test_gpt3_windowed_shard_full_size():
         Z.zero_adam_shard_step(inp["reps"], b - a, 1.0, inp["master"][a:], inp["m"][a:], inp["v"][a:],
                                h, out=d_slot[a:])
     torch.cuda.synchronize()
-    reps_win = lambda a, b: _bits_to_np(inp["reps"][:, a:b].contiguous(), "bf16")
+    reps_win = lambda a, b: _bits_to_np(_rows(inp["reps"], a, b), "bf16")
     _check_windows(w, wins, before, reps_win, inp["master"], inp["m"], inp["v"], d_slot, hp, 1.0,
                    "bf16", rep_offset=lambda a: a % W)
-    del inp, d_slot
+    del inp, d_slot, views, storage
     _free()

@@ -3,7 +3,7 @@
 Same recipe as ``workloads.host`` (master, replicas 0..R-1 with any injected +inf, then warm m, v),
 drawn with a seeded ``torch.Generator`` on the device (Philox), so a multi-GB shard never crosses
 PCIe. 16-bit replicas are torch's conversions of fp32 draws. Replicas are one [R, size] tensor (one
-allocation, rows contiguous).
+allocation, rows contiguous), or a list of R row tensors when the caller supplies the storage.
 """
 
 from __future__ import annotations
@@ -23,8 +23,17 @@ def generator(seed: int, device) -> torch.Generator:
     return g
 
 
-def master_shard(w: Workload, begin: int, size: int, gen, device) -> torch.Tensor:
-    x = torch.randn(size, generator=gen, device=device, dtype=torch.float32)
+def _new(empty, name: str, size: int, dtype, device) -> torch.Tensor:
+    if empty is None:
+        return torch.empty(size, dtype=dtype, device=device)
+    t = empty(name, size, dtype)
+    assert t.shape == (size,) and t.dtype == dtype, (name, t.shape, t.dtype)
+    return t
+
+
+def master_shard(w: Workload, begin: int, size: int, gen, device, empty=None) -> torch.Tensor:
+    x = _new(empty, "master", size, torch.float32, device)
+    torch.randn(size, generator=gen, out=x)
     x.mul_(w.master_std)
     if w.model is not None:
         end = begin + size
@@ -37,9 +46,12 @@ def master_shard(w: Workload, begin: int, size: int, gen, device) -> torch.Tenso
     return x
 
 
-def replicas(w: Workload, size: int, valid: int, gen, device, reps: int | None = None) -> torch.Tensor:
+def replicas(w: Workload, size: int, valid: int, gen, device, reps: int | None = None, empty=None):
     r = w.reps if reps is None else reps
-    out = torch.empty((r, size), dtype=_DT[w.rep_dtype], device=device)
+    if empty is None:
+        out = torch.empty((r, size), dtype=_DT[w.rep_dtype], device=device)
+    else:
+        out = [_new(empty, f"rep{k}", size, _DT[w.rep_dtype], device) for k in range(r)]
     for k in range(r):
         x = torch.randn(size, generator=gen, device=device, dtype=torch.float32)
         x.mul_(w.rep_std * (w.loss_scale if w.rep_dtype == "f16" else 1.0))
@@ -57,9 +69,9 @@ def replicas(w: Workload, size: int, valid: int, gen, device, reps: int | None =
     return out
 
 
-def warm_state(w: Workload, size: int, valid: int, gen, device):
-    m = torch.zeros(size, dtype=torch.float32, device=device)
-    v = torch.zeros(size, dtype=torch.float32, device=device)
+def warm_state(w: Workload, size: int, valid: int, gen, device, empty=None):
+    m = _new(empty, "m", size, torch.float32, device).zero_()
+    v = _new(empty, "v", size, torch.float32, device).zero_()
     k = w.warm_steps
     if k > 0:
         sg = w.rep_std * math.sqrt(w.reps)
@@ -73,11 +85,15 @@ def warm_state(w: Workload, size: int, valid: int, gen, device):
 
 
 def rank_inputs(w: Workload, begin: int, size: int, valid: int, device="cuda",
-                seed_offset: int = 0, rep_size: int | None = None):
-    """dict(master, m, v, reps); ``rep_size`` < size draws one replica window (re-read per window)."""
+                seed_offset: int = 0, rep_size: int | None = None, empty=None):
+    """dict(master, m, v, reps); ``rep_size`` < size draws one replica window (re-read per window).
+
+    ``empty(name, numel, dtype)``, when given, supplies each array's storage (names master, m, v,
+    rep0 .. rep{R-1}), for example views of one arena; the values drawn are the same either way.
+    """
     gen = generator(w.seed + seed_offset, device)
-    master = master_shard(w, begin, size, gen, device)
+    master = master_shard(w, begin, size, gen, device, empty)
     rs = size if rep_size is None else rep_size
-    reps = replicas(w, rs, min(valid, rs), gen, device)
-    m, v = warm_state(w, size, valid, gen, device)
+    reps = replicas(w, rs, min(valid, rs), gen, device, empty=empty)
+    m, v = warm_state(w, size, valid, gen, device, empty)
     return {"master": master, "m": m, "v": v, "reps": reps}

@@ -21,7 +21,7 @@ __all__ = [
     "ZERO_MAX_REPLICAS", "ZERO_MAX_SHARDS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
     "ZERO_ADAMW", "ZERO_ADAM_L2", "adam_hparams",
     "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_choose_stage",
-    "zero_adam_derive",
+    "zero_adam_derive", "ZeroArenaArray", "zero_arena_layout", "arena",
     "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
     "zero_gather_params", "zero_host_adam_step", "zero_offload_step",
     "zero_status_str", "zero_last_error",
@@ -74,6 +74,11 @@ class ZeroOffloadBuffers(ctypes.Structure):
                 ("reserved", ctypes.c_uint32), ("h2d_stream", ctypes.c_void_p)]
 
 
+class ZeroArenaArray(ctypes.Structure):
+    _fields_ = [("bytes", ctypes.c_uint64), ("hot_offset", ctypes.c_uint64), ("group", ctypes.c_uint32),
+                ("elem_bytes", ctypes.c_uint32)]
+
+
 class ZeroAdamScalars(ctypes.Structure):
     _fields_ = [(k, ctypes.c_float) for k in ("b1", "b2", "c1", "c2", "ss", "bc", "e", "dec", "w")]
 
@@ -108,6 +113,7 @@ def lib() -> ctypes.CDLL:
             "zero_stage_bytes": [P(ZeroPlan), u32, u32, u32, u32, P(u64)],
             "zero_choose_stage": [P(ZeroPlan), u64, u32, u32, u32, P(ZeroStageChoice)],
             "zero_adam_derive": [P(ZeroAdamHParams), P(ZeroAdamScalars)],
+            "zero_arena_layout": [P(ZeroArenaArray), u32, P(u64), P(u64)],
             "zero_reduce_shard": [P(_GradSrc), u64, vp, vp, vp, ctypes.c_double, vp],
             "zero_shard_sqnorm": [vp, u64, ctypes.c_double, vp, vp, vp],
             "zero_adam_shard_step": [P(_GradSrc), u64, ctypes.c_float, vp, vp, vp,
@@ -181,6 +187,32 @@ def zero_adam_derive(hp: ZeroAdamHParams) -> ZeroAdamScalars:
     out = ZeroAdamScalars()
     _check(lib().zero_adam_derive(ctypes.byref(hp), ctypes.byref(out)), "zero_adam_derive")
     return out
+
+
+def zero_arena_layout(arrays) -> tuple[list[int], int]:
+    """arrays: sequence of (bytes, hot_offset, group, elem_bytes) -> (byte offsets, total bytes)."""
+    n = len(arrays)
+    arr = (ZeroArenaArray * max(n, 1))(*[ZeroArenaArray(int(b), int(h), int(g), int(e))
+                                         for b, h, g, e in arrays])
+    offs = (ctypes.c_uint64 * max(n, 1))()
+    total = ctypes.c_uint64()
+    _check(lib().zero_arena_layout(arr, n, offs, ctypes.byref(total)), "zero_arena_layout")
+    return [int(offs[i]) for i in range(n)], int(total.value)
+
+
+def arena(specs, device="cuda"):
+    """One device allocation holding every array of ``specs`` where zero_arena_layout places it.
+
+    specs: sequence of (name, numel, dtype, group, hot_elem): hot_elem is the element at which the
+    kernels' walk over the array starts (0, or r*S for rank r's slot in a gathered buffer). Returns
+    (storage, {name: 1-D view}); the views live as long as the storage.
+    """
+    specs = list(specs)
+    es = [torch.empty(0, dtype=dt).element_size() for _, _, dt, _, _ in specs]
+    offs, total = zero_arena_layout([(n * e, h * e, g, e) for (_, n, _, g, h), e in zip(specs, es)])
+    storage = torch.empty(max(total, 1), dtype=torch.uint8, device=device)
+    views = {name: storage[o:o + n * e].view(dt) for (name, n, dt, _, _), o, e in zip(specs, offs, es)}
+    return storage, views
 
 
 # ------------------------------------------------------------------------------ device calls

@@ -21,17 +21,20 @@ Prints one JSON line (see the fields below). Flags:
   --copy-calib MB  also run a plain device copy of MB MiB 5 times (for counter calibration)
   --summarize      (no GPU) turn the rocprofv3 CSVs of the profile commands into the summaries
                    under profiles/ and exit
-  --profile-commands  print the three rocprofv3 commands for --workload and exit
+  --profile-commands  print the three rocprofv3 commands for --workload, and the same bench
+                   command untraced, and exit
 
 The kernel-trace summary and the two counter passes (FETCH_SIZE, then WRITE_SIZE) are taken by the
 commands --profile-commands prints; their CSVs land in gpurun_out/prof_<workload>_{trace,fetch,write}
-and their console output in the .log file of the same name.
+and their console output in the .log file of the same name. The untraced run (prof_<workload>_plain.log)
+gives the event figure without the profiler's per-dispatch cost, for comparison in the summary.
 """
 
 from __future__ import annotations
 
 import argparse
 import dataclasses
+import gc
 import hashlib
 import json
 import math
@@ -45,8 +48,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sharded Adam step params/s per GPU + achieved HBM GB/s vs peak (7B, Nd=8)"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRCS = [os.path.join(ROOT, "zero_partition_plan_amd", "csrc", f)
-               for f in ("zero_step.hip", "zero_gather.hip", "zero_device.h")]
+_CSRC = os.path.join(ROOT, "zero_partition_plan_amd", "csrc")
+# the device sources each kernel is built from
+KERNEL_SRCS = {k: [os.path.join(_CSRC, f) for f in fs] for k, fs in {
+    "k_adam_step": ("zero_step.hip", "zero_device.h"),
+    "k_reduce": ("zero_step.hip", "zero_device.h"),
+    "k_gather": ("zero_gather.hip", "zero_device.h"),
+}.items()}
 PROFILES = os.path.join(ROOT, "profiles")
 CALIB_MIB = 1024
 
@@ -75,10 +83,11 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
-    """sha256[:16] over every device source: a counter summary is used only for this exact code."""
+def kernel_hash(kernel: str) -> str:
+    """sha256[:16] over the device sources of ``kernel``: a counter summary is used only for the
+    exact code it was taken on."""
     h = hashlib.sha256()
-    for f in KERNEL_SRCS:
+    for f in KERNEL_SRCS[kernel]:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
@@ -129,6 +138,18 @@ def launch_elems(workload: str) -> int:
     return min(shard_elems(w), w.window or shard_elems(w))
 
 
+def launches_per_step(workload: str) -> int:
+    """Library calls one step makes (timed spans), for reserving their events up front."""
+    from workloads import WORKLOADS
+    if workload == "gather7b":
+        return GATHER_LAYERS
+    if workload == "offload7b":
+        return 1
+    w = WORKLOADS["llama13b" if workload.startswith("llama13b") else workload]
+    S = shard_elems(w)
+    return 2 if workload.startswith("llama13b") else -(-S // (w.window or S))
+
+
 def algorithmic_bytes_per_launch(workload: str) -> float:
     k = dominant_kernels(workload)[0]
     return float(kernel_bytes_per_elem(workload)[k]) * launch_elems(workload)
@@ -142,7 +163,7 @@ def recorded_traffic(workload: str, kernel: str):
     text = open(path).read()
     m_hash = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
     m_bytes = re.search(r"HBM bytes per launch \(calibrated\):\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash(kernel):
         return None
     return float(m_bytes.group(1))
 
@@ -150,7 +171,8 @@ def recorded_traffic(workload: str, kernel: str):
 # ----------------------------------------------------------------------------- profiles
 
 def profile_dirs(workload: str) -> dict:
-    return {k: os.path.join("gpurun_out", f"prof_{workload}_{k}") for k in ("trace", "fetch", "write")}
+    return {k: os.path.join("gpurun_out", f"prof_{workload}_{k}")
+            for k in ("trace", "fetch", "write", "plain")}
 
 
 def profile_commands(workload: str) -> dict:
@@ -163,6 +185,7 @@ def profile_commands(workload: str) -> dict:
                  f"{run} --steps 3 --warmup 1 --cpu-seconds 0 --copy-calib {CALIB_MIB}",
         "write": f"rocprofv3 --pmc WRITE_SIZE -T -d {d['write']} -o pmc -f csv -- "
                  f"{run} --steps 3 --warmup 1 --cpu-seconds 0 --copy-calib {CALIB_MIB}",
+        "plain": f"{run} --steps 10 --warmup 2 --cpu-seconds 0",
     }
 
 
@@ -223,6 +246,11 @@ def summarize(workload: str):
         rl = json.loads(bench_line)["roofline"]
         lines += ["", f"bench.py's own HIP-event figure in the same run: {rl['avg_launch_ms']:.4f} ms "
                       f"per launch of {rl['kernel']} ({rl['achieved']:.0f} GB/s algorithmic)."]
+    plain_line = _logged(dirs["plain"], r"(\{\"metric\".*\})")
+    if plain_line:
+        rl = json.loads(plain_line)["roofline"]
+        lines += [f"The same bench command without the profiler (`{cmds['plain']}`): "
+                  f"{rl['avg_launch_ms']:.4f} ms per launch ({rl['achieved']:.0f} GB/s algorithmic)."]
     lines += ["", "Kernels other than the library's are the seeded input generators (torch) that run "
               "before the timed region."]
     out = os.path.join(PROFILES, f"{kernels[0]}_{workload}_trace.md")
@@ -489,16 +517,27 @@ def hparams(st):
 
 
 class Spans:
-    """HIP-event pairs around library calls, per kernel name, on the stream the library uses."""
+    """HIP-event pairs around library calls, per kernel name, on the stream the library uses.
 
-    def __init__(self, on: bool):
+    The events are created before the timed region (``reserve`` pairs, more in blocks if needed),
+    so that a span costs the host two event records and nothing else: with launches of ~0.1 ms the
+    host must stay ahead of the GPU, or the GPU idles inside a span and the span overstates the
+    kernel's time.
+    """
+
+    def __init__(self, on: bool, reserve: int = 0):
         self.on = on
         self.pairs = {}
+        self.pool = [(new_event(), new_event()) for _ in range(reserve)] if on else []
+        self.used = 0
 
     def __call__(self, name, fn):
         if not self.on:
             return fn()
-        a, b = new_event(), new_event()
+        if self.used == len(self.pool):
+            self.pool += [(new_event(), new_event()) for _ in range(256)]
+        a, b = self.pool[self.used]
+        self.used += 1
         a.record()
         fn()
         b.record()
@@ -513,11 +552,15 @@ def step_fused(st, spans):
     import zero_partition_plan_amd as Z
     inp, S, W = st["inp"], st["S"], st["w"].window
     h = hparams(st)
-    for a in range(0, S, W or S):
-        b = min(S, a + (W or S))
+    if W is None:                      # one launch over the whole shard: no views to make
         spans("k_adam_step", lambda: Z.zero_adam_shard_step(
-            inp["reps"], b - a, 1.0, inp["master"][a:], inp["m"][a:], inp["v"][a:], h,
-            out=st["slot"][a:]))
+            inp["reps"], S, 1.0, inp["master"], inp["m"], inp["v"], h, out=st["slot"]))
+    else:
+        for a in range(0, S, W):
+            b = min(S, a + W)
+            spans("k_adam_step", lambda: Z.zero_adam_shard_step(
+                inp["reps"], b - a, 1.0, inp["master"][a:], inp["m"][a:], inp["v"][a:], h,
+                out=st["slot"][a:]))
     st["t"] += 1
 
 
@@ -659,7 +702,7 @@ def main(argv=None):
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
-    log(f"kernel source sha256[:16] {kernel_hash()}")
+    log(f"kernel source sha256[:16] {kernel_hash(dominant_kernels(args.workload)[0])}")
 
     if args.workload == "gather7b":
         st, step = setup_gather(), step_gather
@@ -675,9 +718,11 @@ def main(argv=None):
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done; timing {args.steps} steps")
 
-    spans = Spans(True)
+    spans = Spans(True, reserve=args.steps * launches_per_step(args.workload))
     t_start, t_end = new_event(), new_event()
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()                       # no collector pause while the host enqueues the timed steps
     wall0 = time.perf_counter()
     t_start.record()
     for _ in range(args.steps):
@@ -685,6 +730,7 @@ def main(argv=None):
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     params_per_s = S * args.steps / (total_ms / 1e3)

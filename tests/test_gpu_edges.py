@@ -115,10 +115,11 @@ def test_fewer_elements_than_ranks(n, nd):
 
 
 def test_shard_past_2_pow_33_elements():
-    """One call over n = 2^33 + 5000 elements (16,777,225 tiles: two grids), one bf16 replica,
-    bf16 output: about 137 GB of device memory."""
+    """One call over n = 2^33 + 5000 elements: 33,554,451 whole 256-element tiles in three grids of
+    at most 2^24 blocks, and a 136-element remainder taken by the last grid's extra block. One bf16
+    replica, bf16 output: about 137 GB of device memory."""
     n = (1 << 33) + 5000
-    tile = 512
+    tile = 256                                        # Adam kernel tile
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     banner(f"huge shard n={n}")
@@ -129,8 +130,8 @@ def test_shard_past_2_pow_33_elements():
     m = torch.zeros(n, device=DEV)
     v = torch.zeros(n, device=DEV)
     out = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
-    boundary = (1 << 24) * tile                       # first element of the second grid
-    wins = [(0, 1 << 16), (boundary - 4099, boundary + 4099), ((1 << 32) - 777, (1 << 32) + 777),
+    boundary = (1 << 24) * tile                       # first element of the second grid (2^32)
+    wins = [(0, 1 << 16), (boundary - 4099, boundary + 4099), (2 * boundary - 777, 2 * boundary + 777),
             (n - 70_000, n)]
     before = {w: bits32(master[w[0]:w[1]]).view(np.float32) for w in wins}
     Z.zero_adam_shard_step([rep], n, 1.0, master, m, v, Z.adam_hparams(step=1, **HP), out=out)

@@ -19,7 +19,7 @@ from workloads.extremes import EXTREME_CASES, f16_all_patterns, f32_patterns, mi
 
 pytestmark = pytest.mark.gpu
 
-TILE = 512  # elements per block tile of the Adam and reduce kernels (64 threads x 4 x 2)
+TILE = 512  # elements per reduce-kernel tile (64 threads x 4 x 2); two Adam-kernel tiles of 256
 
 
 def _reps_np(rng, R, n, dtype, std=1e-3, valid=None):

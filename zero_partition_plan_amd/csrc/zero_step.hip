@@ -4,8 +4,9 @@
 // shaped for MFMA. A tile is SUB groups of 4 consecutive elements per thread, the groups spaced
 // block*4 elements apart, so every load instruction of a wave covers one contiguous 1 KiB (fp32)
 // or 512 B (16-bit) run. Loads and stores are non-temporal: every byte is touched once per step.
-// The Adam kernel runs one single-wave tile per block over the aligned whole tiles of the shard;
-// a separate per-element kernel takes the ragged end and arrays that are not 16-byte aligned.
+// The Adam kernel runs one single-wave tile per block over the aligned whole tiles of the shard,
+// plus one block for a partial last tile; a separate per-element kernel takes arrays that are not
+// 16-byte aligned.
 // Measured on MI355X, one-wave blocks with one group per lane (a 256-element tile) moved this
 // 15-stream read/write mix fastest: faster than 2 or 4 groups per lane, 128- or 256-thread blocks,
 // grid-stride (persistent) launches and software-pipelined multi-tile blocks.
@@ -176,20 +177,45 @@ __device__ __forceinline__ void adam1(float acc, float& p, float& m, float& v, c
 // fused step: replica sum -> Adam/AdamW on master/m/v -> 16-bit cast into the rank's slot
 //
 // Two kernels share the arithmetic. k_adam_step covers whole tiles of arrays that are all 16-byte
-// aligned (8-byte for 16-bit arrays) with vector loads and stores, one tile per block; it holds no
-// per-element path, so its register budget stays small and more waves fit on a SIMD. k_adam_tail
-// covers any other element range (the ragged end of a shard, or a shard whose arrays are not
-// aligned) one element per thread.
+// aligned (8-byte for 16-bit arrays) with vector loads and stores, one tile per block. When the
+// shard ends in a partial tile, the TAIL variant's grid has one block more, which walks that
+// remainder (fewer than one tile) element by element, so a ragged shard still takes one launch.
+// k_adam_tail covers the arrays that are not aligned, one element per thread.
 
-template <int RDT, int ODT, bool L2, int RFIX, bool SKIP>
+// element i of the update: replica sum, Adam, 16-bit cast (any alignment)
+template <int RDT, int ODT, bool L2>
+__device__ __forceinline__ void adam_elem(const RepPtrs& reps, int nrep, uint64_t i,
+                                          const StepScalars& sc, float* __restrict__ P,
+                                          float* __restrict__ M, float* __restrict__ V,
+                                          void* __restrict__ out) {
+  const float a = sum_reps1<RDT>(reps, nrep, i);
+  float p = P[i], m = M[i], v = V[i];
+  adam1<L2>(a, p, m, v, sc);
+  P[i] = p;
+  M[i] = m;
+  V[i] = v;
+  if constexpr (ODT != ZERO_F32) static_cast<uint16_t*>(out)[i] = to_out1<ODT>(p);
+}
+
+template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL>
 __global__ __launch_bounds__(kAdamBlock) void k_adam_step(
     RepPtrs reps, int nrep, uint64_t first_tile, StepScalars sc, float* __restrict__ P,
     float* __restrict__ M, float* __restrict__ V, void* __restrict__ out,
-    const int32_t* __restrict__ skip) {
-  // One tile per block and the grid is exactly the tile count: no loop bound and no per-block
-  // bound check to wait for, so a block's first loads issue right after its arguments arrive.
+    const int32_t* __restrict__ skip, uint64_t n) {
+  // One tile per block and the grid is exactly the tile count (plus the remainder block with
+  // TAIL): no loop bound and no per-block bound check to wait for, so a block's first loads issue
+  // right after its arguments arrive.
   if constexpr (SKIP) {
     if (*skip != 0) return;
+  }
+  constexpr uint64_t kTileElems = (uint64_t)kAdamBlock * 4 * ZERO_ADAM_SUB;
+  if constexpr (TAIL) {
+    if (blockIdx.x == gridDim.x - 1) {   // elements [tile start, n): fewer than one tile
+#pragma unroll 1   // kept rolled: its registers must not raise the whole-tile path's budget
+      for (uint64_t i = (first_tile + blockIdx.x) * kTileElems + threadIdx.x; i < n; i += kAdamBlock)
+        adam_elem<RDT, ODT, L2>(reps, nrep, i, sc, P, M, V, out);
+      return;
+    }
   }
   constexpr int SUB = ZERO_ADAM_SUB;
   constexpr uint64_t kTile = (uint64_t)kAdamBlock * 4 * SUB;
@@ -233,15 +259,8 @@ __global__ __launch_bounds__(kBlock) void k_adam_tail(RepPtrs reps, int nrep, ui
                                                       const int32_t* __restrict__ skip) {
   if (skip != nullptr && *skip != 0) return;
   for (uint64_t i = begin + (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
-       i += (uint64_t)gridDim.x * kBlock) {
-    const float a = sum_reps1<RDT>(reps, nrep, i);
-    float p = P[i], m = M[i], v = V[i];
-    adam1<L2>(a, p, m, v, sc);
-    P[i] = p;
-    M[i] = m;
-    V[i] = v;
-    if constexpr (ODT != ZERO_F32) static_cast<uint16_t*>(out)[i] = to_out1<ODT>(p);
-  }
+       i += (uint64_t)gridDim.x * kBlock)
+    adam_elem<RDT, ODT, L2>(reps, nrep, i, sc, P, M, V, out);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -439,27 +458,40 @@ struct AdamArgs {
   const int32_t* skip;
   unsigned tail_grid;
   hipStream_t stream;
+  bool fused_tail;      // aligned shard with a partial last tile: k_adam_step's extra block takes it
 };
+
+template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL>
+void launch_adam_grid(const AdamArgs& a, uint64_t t0, uint64_t blocks) {
+  hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, SKIP, TAIL>), dim3((unsigned)blocks),
+                     dim3(kAdamBlock), 0, a.stream, a.reps, a.nrep, t0, a.sc, a.P, a.M, a.V, a.out,
+                     a.skip, a.n);
+}
 
 template <int RDT, int ODT, bool L2, int RFIX>
 void launch_adam(const AdamArgs& a) {
-  // grids of at most kMaxGrid tiles, each told where its first tile is
-  for (uint64_t t0 = 0; t0 < a.ntiles; t0 += kMaxGrid) {
+  // Grids of at most kMaxGrid tiles, each told where its first tile is. A partial last tile of an
+  // aligned shard rides on the last grid as one extra block (TAIL); a shard shorter than one tile
+  // is then a grid of that block alone.
+  const bool tail = a.fused_tail;
+  uint64_t t0 = 0;
+  do {
     const uint64_t g = a.ntiles - t0 < kMaxGrid ? a.ntiles - t0 : kMaxGrid;
-    if (a.skip != nullptr)
-      hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, true>), dim3((unsigned)g),
-                         dim3(kAdamBlock), 0, a.stream, a.reps, a.nrep, t0, a.sc, a.P, a.M, a.V,
-                         a.out, a.skip);
-    else
-      hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, false>), dim3((unsigned)g),
-                         dim3(kAdamBlock), 0, a.stream, a.reps, a.nrep, t0, a.sc, a.P, a.M, a.V,
-                         a.out, a.skip);
-  }
+    const bool last = t0 + g == a.ntiles;
+    if (last && tail) {
+      if (a.skip != nullptr) launch_adam_grid<RDT, ODT, L2, RFIX, true, true>(a, t0, g + 1);
+      else launch_adam_grid<RDT, ODT, L2, RFIX, false, true>(a, t0, g + 1);
+    } else if (g > 0) {
+      if (a.skip != nullptr) launch_adam_grid<RDT, ODT, L2, RFIX, true, false>(a, t0, g);
+      else launch_adam_grid<RDT, ODT, L2, RFIX, false, false>(a, t0, g);
+    }
+    t0 += g;
+  } while (t0 < a.ntiles);
 }
 
 template <int RDT, int ODT, bool L2>
 void adam_kernels(const AdamArgs& a) {
-  if (a.ntiles > 0) {
+  if (a.ntiles > 0 || a.fused_tail) {
     switch (a.nrep) {
       case 1: launch_adam<RDT, ODT, L2, 1>(a); break;
       case 8: launch_adam<RDT, ODT, L2, 8>(a); break;
@@ -468,7 +500,7 @@ void adam_kernels(const AdamArgs& a) {
       default: launch_adam<RDT, ODT, L2, 0>(a); break;
     }
   }
-  if (a.tail_begin < a.n)
+  if (!a.fused_tail && a.tail_begin < a.n)
     hipLaunchKernelGGL((k_adam_tail<RDT, ODT, L2>), dim3(a.tail_grid), dim3(kBlock), 0, a.stream,
                        a.reps, a.nrep, a.tail_begin, a.n, a.sc, a.P, a.M, a.V, a.out, a.skip);
 }
@@ -649,7 +681,7 @@ zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float gra
   AdamArgs a{rep_ptrs(src), (int)src->count, ntiles, tail_begin, n,
              StepScalars{grad_scale, k.b1, k.b2, k.c1, k.c2, k.ss, k.bc, k.e, k.dec, k.w},
              master, m, v, out_param, d_skip, (unsigned)tail_grid,
-             static_cast<hipStream_t>(stream)};
+             static_cast<hipStream_t>(stream), vec && tail_n > 0};
   const int odt = out_param ? out_dtype : ZERO_F32;
   const bool l2 = hp->wd_mode == ZERO_ADAM_L2;
   (void)hipGetLastError();

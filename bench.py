@@ -713,9 +713,12 @@ def main(argv=None):
         step = step_two_pass if args.workload.startswith("llama13b") else step_fused
     w, S = st["w"], st["S"]
 
+    nvtx = torch.cuda.nvtx             # roctx ranges: phases show up in a marker trace
+    nvtx.range_push(f"warmup {args.workload}")
     for _ in range(args.warmup):
         step(st, Spans(False))
     torch.cuda.synchronize()
+    nvtx.range_pop()
     log(f"warmup {args.warmup} done; timing {args.steps} steps")
 
     spans = Spans(True, reserve=args.steps * launches_per_step(args.workload))
@@ -723,6 +726,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     gc.collect()
     gc.disable()                       # no collector pause while the host enqueues the timed steps
+    nvtx.range_push(f"timed {args.steps} steps {args.workload}")
     wall0 = time.perf_counter()
     t_start.record()
     for _ in range(args.steps):
@@ -730,6 +734,7 @@ def main(argv=None):
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    nvtx.range_pop()
     gc.enable()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
@@ -782,11 +787,13 @@ def main(argv=None):
         log(f"cold launches: median {cold['median_ms']:.4f} ms -> {cold['gbs_at_median']:.0f} GB/s")
     context = None
     if args.workload == "llama7b" and not args.no_context:
+        nvtx.range_push("context legs")
         context = {"copy_ceiling": copy_ceiling()}
         log(f"copy ceiling: {context['copy_ceiling']['gbs']:.0f} GB/s")
         if args.placement == "arena":
             context["placement"] = placement_context(args.workload)
             log(f"separate allocations: {context['placement']['separate_ms_per_step']:.4f} ms per step")
+        nvtx.range_pop()
 
     if args.copy_calib:
         nb = args.copy_calib << 20

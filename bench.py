@@ -328,7 +328,9 @@ def setup(name: str, placement: str = "arena"):
     storage, views = None, None
     if placement == "arena":
         storage, views = Z.arena(step_arrays(w, S, begin, plan.padded_n, two_pass), device=dev)
-        log(f"arena: {storage.numel() / 2**30:.2f} GiB for {len(views)} arrays")
+        log(f"arena: {storage.numel() / 2**30:.2f} GiB for {len(views)} arrays, "
+            f"{'physically contiguous' if storage.zero_arena_contiguous else 'not contiguous'}")
+        placement = "arena, contiguous" if storage.zero_arena_contiguous else "arena"
     empty = (lambda nm, n, dt: views[nm]) if views else None
     inp = D.rank_inputs(w, begin, S, valid, device=dev, rep_size=w.window, empty=empty)
     out_t = torch.float16 if w.out_dtypes[0] == "f16" else torch.bfloat16

@@ -155,6 +155,19 @@ typedef struct {
 zero_status zero_arena_layout(const zero_arena_array* arrays, uint32_t count, uint64_t* offsets,
                               uint64_t* total_bytes);
 
+/* Device memory for an arena: total_bytes from zero_arena_layout. Asks the device for physically
+ * contiguous memory, so that the layout's offsets hold in physical addresses too; if it cannot
+ * give that much contiguous memory, makes an ordinary device allocation instead.
+ * *d_ptr receives the allocation (NULL for bytes == 0), *contiguous (nullable) 1 or 0 for which
+ * kind it is. The caller owns it and releases it with zero_arena_free. These are the library's only
+ * allocations; no step allocates. Host call on the current device. Errors: d_ptr NULL ->
+ * ZERO_E_INVAL; no device memory of that size -> ZERO_E_HIP. */
+zero_status zero_arena_alloc(uint64_t bytes, void** d_ptr, int32_t* contiguous);
+
+/* Releases an allocation of zero_arena_alloc (NULL is a no-op). The device must have finished
+ * with it (synchronise first). Errors: a HIP failure -> ZERO_E_HIP. */
+zero_status zero_arena_free(void* d_ptr);
+
 /* The fp32 constants of step hp->step, each formed in fp64 and rounded once:
  * b1 = f32(beta1), b2 = f32(beta2), c1 = f32(1-beta1), c2 = f32(1-beta2),
  * ss = f32(lr / (1 - pow(beta1, t))), bc = f32(sqrt(1 - pow(beta2, t))), e = f32(eps),

@@ -21,7 +21,8 @@ __all__ = [
     "ZERO_MAX_REPLICAS", "ZERO_MAX_SHARDS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
     "ZERO_ADAMW", "ZERO_ADAM_L2", "adam_hparams",
     "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_choose_stage",
-    "zero_adam_derive", "ZeroArenaArray", "zero_arena_layout", "arena",
+    "zero_adam_derive", "ZeroArenaArray", "zero_arena_layout", "zero_arena_alloc", "zero_arena_free",
+    "arena",
     "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
     "zero_gather_params", "zero_host_adam_step", "zero_offload_step",
     "zero_status_str", "zero_last_error",
@@ -114,6 +115,8 @@ def lib() -> ctypes.CDLL:
             "zero_choose_stage": [P(ZeroPlan), u64, u32, u32, u32, P(ZeroStageChoice)],
             "zero_adam_derive": [P(ZeroAdamHParams), P(ZeroAdamScalars)],
             "zero_arena_layout": [P(ZeroArenaArray), u32, P(u64), P(u64)],
+            "zero_arena_alloc": [u64, P(vp), P(i32)],
+            "zero_arena_free": [vp],
             "zero_reduce_shard": [P(_GradSrc), u64, vp, vp, vp, ctypes.c_double, vp],
             "zero_shard_sqnorm": [vp, u64, ctypes.c_double, vp, vp, vp],
             "zero_adam_shard_step": [P(_GradSrc), u64, ctypes.c_float, vp, vp, vp,
@@ -200,17 +203,55 @@ def zero_arena_layout(arrays) -> tuple[list[int], int]:
     return [int(offs[i]) for i in range(n)], int(total.value)
 
 
-def arena(specs, device="cuda"):
+def zero_arena_alloc(nbytes: int) -> tuple[int | None, bool]:
+    """(device pointer, physically contiguous?) of a new allocation on the current device."""
+    ptr, contig = ctypes.c_void_p(), ctypes.c_int32()
+    _check(lib().zero_arena_alloc(nbytes, ctypes.byref(ptr), ctypes.byref(contig)), "zero_arena_alloc")
+    return ptr.value, bool(contig.value)
+
+
+def zero_arena_free(ptr: int | None):
+    _check(lib().zero_arena_free(ptr), "zero_arena_free")
+
+
+class _ArenaMemory:
+    """Owner of one zero_arena_alloc allocation, handed to torch as a uint8 array. torch keeps this
+    object alive while any tensor on the memory lives, and the memory is freed with it."""
+
+    def __init__(self, nbytes: int):
+        self.ptr, self.contiguous = zero_arena_alloc(nbytes)
+        self.__cuda_array_interface__ = {"shape": (nbytes,), "typestr": "|u1", "strides": None,
+                                         "data": (self.ptr, False), "version": 2}
+
+    def __del__(self):
+        if getattr(self, "ptr", None):
+            zero_arena_free(self.ptr)
+            self.ptr = None
+
+
+def arena(specs, device="cuda", contiguous: bool = True):
     """One device allocation holding every array of ``specs`` where zero_arena_layout places it.
 
     specs: sequence of (name, numel, dtype, group, hot_elem): hot_elem is the element at which the
-    kernels' walk over the array starts (0, or r*S for rank r's slot in a gathered buffer). Returns
-    (storage, {name: 1-D view}); the views live as long as the storage.
+    kernels' walk over the array starts (0, or r*S for rank r's slot in a gathered buffer). With
+    ``contiguous`` (device memory only) the allocation comes from zero_arena_alloc, physically
+    contiguous when the device can give it; otherwise from torch. Returns (storage, {name: 1-D
+    view}); the views live as long as the storage, and ``storage.zero_arena_contiguous`` says
+    whether the memory is physically contiguous.
     """
     specs = list(specs)
     es = [torch.empty(0, dtype=dt).element_size() for _, _, dt, _, _ in specs]
     offs, total = zero_arena_layout([(n * e, h * e, g, e) for (_, n, _, g, h), e in zip(specs, es)])
-    storage = torch.empty(max(total, 1), dtype=torch.uint8, device=device)
+    dev = torch.device(device)
+    if contiguous and dev.type == "cuda":
+        with torch.cuda.device(dev):
+            mem = _ArenaMemory(max(total, 1))
+            storage = torch.as_tensor(mem, device=dev)
+        assert storage.data_ptr() == mem.ptr and storage.numel() == max(total, 1)
+        storage.zero_arena_contiguous = mem.contiguous
+    else:
+        storage = torch.empty(max(total, 1), dtype=torch.uint8, device=dev)
+        storage.zero_arena_contiguous = False
     views = {name: storage[o:o + n * e].view(dt) for (name, n, dt, _, _), o, e in zip(specs, offs, es)}
     return storage, views
 

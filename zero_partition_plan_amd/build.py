@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libzero_shard.so")
 SOURCES = [os.path.join(CSRC, "zero_host.cpp"), os.path.join(CSRC, "zero_step.hip"),
            os.path.join(CSRC, "zero_gather.hip"), os.path.join(CSRC, "zero_host_adam.cpp"),
-           os.path.join(CSRC, "zero_offload.cpp")]
+           os.path.join(CSRC, "zero_offload.cpp"), os.path.join(CSRC, "zero_arena.cpp")]
 
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

@@ -1,0 +1,117 @@
+/* The fused step from plain C on the GPU, through the C ABI only: zero_adam_shard_step on device
+ * buffers must equal zero_reduce_shard (device) followed by zero_host_adam_step (host) on the same
+ * inputs, bit for bit: master, m, v and the bf16 slot. Exits 0 when they match. */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "zero_shard.h"
+
+#define N 100003u /* several tiles and a ragged end */
+#define R 3u
+
+static uint64_t state = 0x9e3779b97f4a7c15ull;
+static float uniform(void) { /* [-1, 1), 24 random bits */
+  state = state * 6364136223846793005ull + 1442695040888963407ull;
+  return (float)((int32_t)(state >> 40) - (1 << 23)) / (float)(1 << 23);
+}
+
+#define HIP(x)                                                                  \
+  do {                                                                          \
+    hipError_t e_ = (x);                                                        \
+    if (e_ != hipSuccess) {                                                     \
+      fprintf(stderr, "%s:%d: %s\n", __FILE__, __LINE__, hipGetErrorString(e_)); \
+      return 2;                                                                 \
+    }                                                                           \
+  } while (0)
+#define ZS(x)                                                                        \
+  do {                                                                               \
+    zero_status s_ = (x);                                                            \
+    if (s_ != ZERO_OK) {                                                             \
+      fprintf(stderr, "%s:%d: %s: %s\n", __FILE__, __LINE__, zero_status_str(s_),   \
+              zero_last_error());                                                    \
+      return 2;                                                                      \
+    }                                                                                \
+  } while (0)
+
+static uint16_t bf16_trunc(float x) { /* an input recipe: replicas as truncated fp32 draws */
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  return (uint16_t)(u >> 16);
+}
+
+int main(void) {
+  static uint16_t reps[R][N], out_dev[N], out_host[N];
+  static float p0[N], m0[N], v0[N], p_dev[N], m_dev[N], v_dev[N], p_host[N], m_host[N], v_host[N], g[N];
+  void* d_reps[R];
+  const void* d_rep_ptrs[R];
+  float *d_p, *d_m, *d_v, *d_g;
+  uint16_t* d_out;
+  zero_grad_src src;
+  zero_adam_hparams hp;
+  uint32_t i, k, bad = 0;
+  const float gs = 0.5f;
+
+  for (k = 0; k < R; ++k)
+    for (i = 0; i < N; ++i) reps[k][i] = bf16_trunc(uniform() * 1e-3f);
+  for (i = 0; i < N; ++i) {
+    p0[i] = uniform() * 0.02f;
+    m0[i] = uniform() * 1e-4f;
+    v0[i] = (uniform() + 1.0f) * 1e-8f;
+  }
+  for (k = 0; k < R; ++k) {
+    HIP(hipMalloc(&d_reps[k], N * 2));
+    HIP(hipMemcpy(d_reps[k], reps[k], N * 2, hipMemcpyHostToDevice));
+    d_rep_ptrs[k] = d_reps[k];
+  }
+  HIP(hipMalloc((void**)&d_p, N * 4));
+  HIP(hipMalloc((void**)&d_m, N * 4));
+  HIP(hipMalloc((void**)&d_v, N * 4));
+  HIP(hipMalloc((void**)&d_g, N * 4));
+  HIP(hipMalloc((void**)&d_out, N * 2));
+  HIP(hipMemcpy(d_p, p0, N * 4, hipMemcpyHostToDevice));
+  HIP(hipMemcpy(d_m, m0, N * 4, hipMemcpyHostToDevice));
+  HIP(hipMemcpy(d_v, v0, N * 4, hipMemcpyHostToDevice));
+
+  src.ptrs = d_rep_ptrs;
+  src.count = R;
+  src.dtype = ZERO_BF16;
+  memset(&hp, 0, sizeof hp);
+  hp.lr = 1e-3; hp.beta1 = 0.9; hp.beta2 = 0.999; hp.eps = 1e-8; hp.weight_decay = 0.01;
+  hp.wd_mode = ZERO_ADAMW; hp.step = 4;
+
+  /* device: fused step; and the reduce pass alone into d_g */
+  ZS(zero_adam_shard_step(&src, N, gs, d_p, d_m, d_v, &hp, d_out, ZERO_BF16, NULL, NULL));
+  ZS(zero_reduce_shard(&src, N, d_g, NULL, NULL, 1.0, NULL));
+  HIP(hipDeviceSynchronize());
+  HIP(hipMemcpy(p_dev, d_p, N * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(m_dev, d_m, N * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(v_dev, d_v, N * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(out_dev, d_out, N * 2, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(g, d_g, N * 4, hipMemcpyDeviceToHost));
+
+  /* host: the same update on the reduced gradient */
+  memcpy(p_host, p0, sizeof p0);
+  memcpy(m_host, m0, sizeof m0);
+  memcpy(v_host, v0, sizeof v0);
+  ZS(zero_host_adam_step(g, N, gs, p_host, m_host, v_host, &hp, out_host, ZERO_BF16, 4));
+
+  for (i = 0; i < N; ++i) {
+    if (memcmp(&p_dev[i], &p_host[i], 4) || memcmp(&m_dev[i], &m_host[i], 4) ||
+        memcmp(&v_dev[i], &v_host[i], 4) || out_dev[i] != out_host[i]) {
+      if (bad < 5) fprintf(stderr, "element %u differs\n", i);
+      ++bad;
+    }
+  }
+  for (k = 0; k < R; ++k) HIP(hipFree(d_reps[k]));
+  HIP(hipFree(d_p));
+  HIP(hipFree(d_m));
+  HIP(hipFree(d_v));
+  HIP(hipFree(d_g));
+  HIP(hipFree(d_out));
+  printf("%u of %u elements differ\n", bad, N);
+  return bad ? 1 : 0;
+}

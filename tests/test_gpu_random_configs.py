@@ -1,0 +1,115 @@
+"""Seeded random configurations of the fused step and the reduce pass against the oracle, beyond
+the parametrized grids: sizes 1..5000 (ragged against every tile), 1..64 replicas of any dtype,
+either output dtype or none, both decay modes, random grad scale and step, per-array element
+offsets (so the vector and per-element paths and the partial last tile all occur), and the skip
+flag. Every fp32 and 16-bit result is compared bit for bit; the squared norm to 1e-10."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import zero_partition_plan_amd as Z
+from gpu_util import DEV, assert_bits_equal, banner, bits16, bits32, dev_f32, dev_rep, f32_bits
+
+pytestmark = pytest.mark.gpu
+
+CASES = 60
+_T16 = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _draw_reps(rng, R, n, dtype):
+    x = (rng.standard_normal((R, n)) * rng.choice([1e-4, 1e-3, 1e-1])).astype(np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+    return (x * np.float32(256.0)).astype(np.float16).view(np.uint16)
+
+
+def _placed(a, off, dtype):
+    """Device copy of ``a`` starting ``off`` elements into its own allocation."""
+    pad = np.zeros(off, a.dtype)
+    if dtype == "f32":
+        return dev_f32(np.concatenate([pad, a]))[off:]
+    return dev_rep(np.concatenate([pad, a]), dtype)[off:]
+
+
+def _config(rng):
+    return dict(
+        n=int(rng.choice([rng.integers(1, 300), rng.integers(300, 5001)])),
+        R=int(rng.choice([1, 2, 3, 7, 8, 9, 16, 17, 33, 64])),
+        rdt=str(rng.choice(["f32", "f16", "bf16"])),
+        odt=[None, "bf16", "f16"][int(rng.integers(0, 3))],
+        mode=str(rng.choice(["adamw", "l2"])),
+        gs=float(np.float32(rng.choice([1.0, 0.5, 2.0 ** -8, float(rng.uniform(0.01, 3))]))),
+        step=int(rng.integers(1, 2000)),
+        wd=float(rng.choice([0.0, 0.01, 0.1])),
+        offs=[int(x) if rng.random() < 0.5 else 0 for x in rng.integers(0, 8, 5)],
+        skip=[None, 0, 1][int(rng.integers(0, 3))],
+    )
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_fused_step(seed):
+    rng = np.random.default_rng(10_000 + seed)
+    c = _config(rng)
+    n, R = c["n"], c["R"]
+    banner(f"random fused step seed={seed} {c}")
+    reps = _draw_reps(rng, R, n, c["rdt"])
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (rng.random(n) * 1e-7).astype(np.float32)
+    o_rep, o_p, o_m, o_v, o_out = c["offs"]
+    d_reps = [_placed(r, o_rep, c["rdt"]) for r in reps]
+    d_p, d_m, d_v = _placed(p, o_p, "f32"), _placed(m, o_m, "f32"), _placed(v, o_v, "f32")
+    d_out = None
+    if c["odt"]:
+        full = torch.full((n + o_out + 3,), -2.0, dtype=_T16[c["odt"]], device=DEV)
+        d_out = full[o_out:o_out + n]
+    skip = None if c["skip"] is None else torch.full((1,), c["skip"], dtype=torch.int32, device=DEV)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=c["wd"], wd_mode=c["mode"],
+              step=c["step"])
+    Z.zero_adam_shard_step(d_reps, n, c["gs"], d_p, d_m, d_v, Z.adam_hparams(**hp), out=d_out, skip=skip)
+    torch.cuda.synchronize()
+    skipped = c["skip"] == 1
+    wp, wm, wv, wo = O.sharded_step(list(reps), c["rdt"], c["gs"], p, m, v, O.AdamHParams(**hp),
+                                    c["odt"], skip=skipped)
+    assert_bits_equal(bits32(d_p), f32_bits(wp), "master")
+    assert_bits_equal(bits32(d_m), f32_bits(wm), "m")
+    assert_bits_equal(bits32(d_v), f32_bits(wv), "v")
+    if c["odt"]:
+        got = bits16(full)
+        fill = bits16(torch.full((1,), -2.0, dtype=_T16[c["odt"]], device=DEV))[0]
+        assert (got[:o_out] == fill).all() and (got[o_out + n:] == fill).all(), "write outside the slot"
+        if skipped:
+            assert (got[o_out:o_out + n] == fill).all(), "skipped step wrote the slot"
+        else:
+            assert_bits_equal(got[o_out:o_out + n], wo, "out")
+
+
+@pytest.mark.parametrize("seed", range(CASES // 2))
+def test_random_reduce(seed):
+    rng = np.random.default_rng(20_000 + seed)
+    n = int(rng.choice([rng.integers(1, 600), rng.integers(600, 9000)]))
+    R = int(rng.choice([1, 2, 5, 8, 16, 31, 64]))
+    rdt = str(rng.choice(["f32", "f16", "bf16"]))
+    off = int(rng.integers(0, 8)) if rng.random() < 0.5 else 0
+    sq_scale = float(rng.choice([1.0, 2.0 ** -16, 0.37]))
+    banner(f"random reduce seed={seed} n={n} R={R} {rdt} off={off}")
+    reps = _draw_reps(rng, R, n, rdt)
+    d_reps = [_placed(r, off, rdt) for r in reps]
+    d_g = torch.empty(n, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    parts = torch.empty(Z.zero_sq_partials_len(n), dtype=torch.float64, device=DEV)
+    sq = torch.empty(1, dtype=torch.float64, device=DEV)
+    Z.zero_reduce_shard(d_reps, n, d_g, flag, parts, sq_scale)
+    Z.zero_shard_sqnorm(None, n, sq_scale, parts, sq)
+    torch.cuda.synchronize()
+    acc = O.replica_sum(list(reps), rdt)
+    assert_bits_equal(bits32(d_g), f32_bits(acc), "reduced gradient")
+    assert int(flag.item()) == int(O.nonfinite_flag(acc))
+    want = O.shard_sqnorm(acc, sq_scale)
+    assert math.isclose(float(sq.item()), want, rel_tol=1e-10, abs_tol=0.0), (float(sq.item()), want)

@@ -1,8 +1,12 @@
-"""Seeded random configurations of the fused step and the reduce pass against the oracle, beyond
-the parametrized grids: sizes 1..5000 (ragged against every tile), 1..64 replicas of any dtype,
-either output dtype or none, both decay modes, random grad scale and step, per-array element
-offsets (so the vector and per-element paths and the partial last tile all occur), and the skip
-flag. Every fp32 and 16-bit result is compared bit for bit; the squared norm to 1e-10."""
+"""Seeded random configurations of the fused step, the reduce pass and the ZeRO-3 gather against
+the oracle, beyond the parametrized grids.
+
+Step and reduce cases draw sizes up to 5000 (ragged against every tile), 1..64 replicas of any
+dtype, either output dtype or none, both decay modes, a random grad scale and step, per-array
+element offsets (so the vector path, the per-element path and the partial last tile all occur) and
+the skip flag. Gather cases draw shard counts and sizes, ranges, element sizes and source and
+output offsets. Every fp32 and 16-bit result is compared bit for bit, the squared norm to 1e-10.
+"""
 
 import math
 
@@ -113,3 +117,31 @@ def test_random_reduce(seed):
     assert int(flag.item()) == int(O.nonfinite_flag(acc))
     want = O.shard_sqnorm(acc, sq_scale)
     assert math.isclose(float(sq.item()), want, rel_tol=1e-10, abs_tol=0.0), (float(sq.item()), want)
+
+
+@pytest.mark.parametrize("seed", range(CASES // 2))
+def test_random_gather(seed):
+    """ZeRO-3 gather: random shard counts and sizes, ranges, element sizes and source / output
+    offsets; shards the range does not touch are passed as NULL."""
+    rng = np.random.default_rng(30_000 + seed)
+    nd = int(rng.choice([1, 2, 3, 8, 13, 64]))
+    S = int(rng.choice([rng.integers(1, 50), rng.integers(50, 3000), rng.integers(3000, 70_000)]))
+    eb = int(rng.choice([2, 4]))
+    src_off, out_off = (int(x) if rng.random() < 0.5 else 0 for x in rng.integers(0, 8, 2))
+    P = nd * S
+    begin = int(rng.integers(0, P))
+    count = int(rng.integers(0, P - begin + 1))
+    banner(f"random gather seed={seed} nd={nd} S={S} eb={eb} [{begin}, {begin + count}) "
+           f"offsets {src_off}/{out_off}")
+    dt_np, dt_t = (np.int16, torch.int16) if eb == 2 else (np.int32, torch.int32)
+    info = np.iinfo(dt_np)
+    host = [rng.integers(info.min, info.max, S, endpoint=True).astype(dt_np) for _ in range(nd)]
+    touched = set(range(begin // S, (begin + count - 1) // S + 1)) if count else set(range(nd))
+    dev = [torch.from_numpy(np.concatenate([np.zeros(src_off, dt_np), h])).to(DEV)[src_off:]
+           if r in touched else None for r, h in enumerate(host)]
+    buf = torch.full((count + out_off + 3,), -5, dtype=dt_t, device=DEV)
+    Z.zero_gather_params(dev, begin, count, buf[out_off:out_off + count])
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    assert (h[:out_off] == -5).all() and (h[out_off + count:] == -5).all(), "write outside out"
+    assert np.array_equal(h[out_off:out_off + count], O.gather_range(host, begin, count))

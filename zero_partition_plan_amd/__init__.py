@@ -224,9 +224,10 @@ class _ArenaMemory:
                                          "data": (self.ptr, False), "version": 2}
 
     def __del__(self):
-        if getattr(self, "ptr", None):
-            zero_arena_free(self.ptr)
-            self.ptr = None
+        # a destructor does not raise; hipFree waits for the device before releasing the memory
+        ptr, self.ptr = getattr(self, "ptr", None), None
+        if ptr and _lib is not None:
+            _lib.zero_arena_free(ptr)
 
 
 def arena(specs, device="cuda", contiguous: bool = True):

@@ -406,6 +406,68 @@ def step_gather(st, spans):
         spans("k_gather", lambda: Z.zero_gather_params(st["shards"], a, b - a, st["bufs"][i % 2]))
 
 
+def gather_prefetch_context(st, tokens: int = 1024, reps: int = 3):
+    """ZeRO-3's layer pipeline on two streams: layer i computes on the current stream while layer i+1
+    is gathered into the other buffer on a second stream. Events make each compute wait for its
+    gather and each gather wait until the compute that last read its buffer is done (the buffer is
+    released). The compute is a stand-in with no model behind it: a bf16 product of a [tokens, 4096]
+    block with the layer's gathered weights viewed as [4096, k]."""
+    import torch
+
+    import zero_partition_plan_amd as Z
+    layers, bufs, shards = st["layers"], st["bufs"], st["shards"]
+    comp, gat = torch.cuda.current_stream(), torch.cuda.Stream()      # default priority
+    x = torch.randn(tokens, 4096, device="cuda").to(torch.bfloat16)
+    flops = sum(2 * tokens * (b - a) for _, a, b in layers)
+
+    def gather(i, stream):
+        _, a, b = layers[i]
+        Z.zero_gather_params(shards, a, b - a, bufs[i % 2], stream=stream)
+
+    def compute(i):
+        _, a, b = layers[i]
+        return torch.mm(x, bufs[i % 2][:b - a].view(4096, -1))
+
+    def pipelined():
+        ready = [torch.cuda.Event(), torch.cuda.Event()]
+        free = [torch.cuda.Event(), torch.cuda.Event()]
+        gat.wait_stream(comp)
+        gather(0, gat)
+        ready[0].record(gat)
+        for i in range(len(layers)):
+            if i + 1 < len(layers):
+                if i >= 1:
+                    gat.wait_event(free[(i + 1) % 2])   # compute i-1 has finished with that buffer
+                gather(i + 1, gat)
+                ready[(i + 1) % 2].record(gat)
+            comp.wait_event(ready[i % 2])
+            compute(i)
+            free[i % 2].record(comp)
+        comp.wait_stream(gat)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = new_event(True), new_event()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    g_ms = timed(lambda: [gather(i, comp) for i in range(len(layers))])
+    c_ms = timed(lambda: [compute(i) for i in range(len(layers))])
+    p_ms = timed(pipelined)
+    return {"gather_only_ms": g_ms, "compute_only_ms": c_ms, "pipelined_ms": p_ms,
+            "gather_hidden": max(0.0, min(1.0, (g_ms + c_ms - p_ms) / g_ms)),
+            "compute_tflops": flops / c_ms / 1e9, "tokens": tokens,
+            "note": "34 layers; compute on the current stream, gathers on a second stream, two "
+                    "alternating layer buffers; gather_hidden = share of the gather time the "
+                    "pipeline hides. The local gather is a full-bandwidth HBM copy and contends with "
+                    "the product for HBM and CUs, so on one GPU the pipeline is slower than gathering "
+                    "then computing; a gather arriving over xGMI would load local HBM far less"}
+
+
 def setup_offload():
     import torch
 
@@ -788,6 +850,14 @@ def main(argv=None):
                         "roofline figures above are warm (back-to-back launches)"}
         log(f"cold launches: median {cold['median_ms']:.4f} ms -> {cold['gbs_at_median']:.0f} GB/s")
     context = None
+    if args.workload == "gather7b" and not args.no_context:
+        nvtx.range_push("context legs")
+        context = {"prefetch": gather_prefetch_context(st)}
+        pf = context["prefetch"]
+        log(f"prefetch pipeline: gathers {pf['gather_only_ms']:.3f} ms, compute {pf['compute_only_ms']:.3f} "
+            f"ms, pipelined {pf['pipelined_ms']:.3f} ms; {100 * pf['gather_hidden']:.0f}% of the gather "
+            f"time hidden")
+        nvtx.range_pop()
     if args.workload == "llama7b" and not args.no_context:
         nvtx.range_push("context legs")
         context = {"copy_ceiling": copy_ceiling()}

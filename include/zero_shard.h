@@ -15,8 +15,9 @@
  * Conventions for every entry point:
  *   - Plain C ABI: sizes are element counts (uint64_t); pointers named d_* or documented as device
  *     pointers must be device memory of the current HIP device; everything else is host memory.
- *   - Ownership: the caller allocates and frees every buffer. The library allocates no memory and
- *     keeps no state except a thread-local error message and a per-device launch-size cache.
+ *   - Ownership: the caller allocates and frees every buffer. No entry point allocates memory except
+ *     zero_arena_alloc, which exists to be asked for it; the library keeps no state except a
+ *     thread-local error message and a per-device launch-size cache.
  *   - Streams: device work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and
  *     never synchronised, except where an entry point says otherwise; device outputs are valid once
  *     the stream reaches that point.

@@ -15,7 +15,6 @@ Pins used:
 
 from __future__ import annotations
 
-import math
 
 import numpy as np
 import torch

@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 import zero_partition_plan_amd as Z
-from gpu_util import DEV, banner, assert_bits_equal
+from gpu_util import DEV, banner
 from workloads import WORKLOADS, layer_ranges
 
 pytestmark = pytest.mark.gpu

@@ -2,7 +2,6 @@
 with eager work and synchronisations between replays, must give the same bits as the same calls
 made eagerly. The step's fp32 constants are fixed at capture (one value of t)."""
 
-import numpy as np
 import pytest
 import torch
 

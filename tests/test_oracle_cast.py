@@ -1,7 +1,6 @@
 """Pins of the oracle's fp32 -> bf16/fp16 casts: brute-force nearest value, torch, special values."""
 
 import numpy as np
-import pytest
 import torch
 
 import oracle as O

@@ -615,16 +615,13 @@ def step_fused(st, spans):
     """One step of a fused workload: one launch per window (one window unless the shard is windowed)."""
     import zero_partition_plan_amd as Z
     inp, S, W = st["inp"], st["S"], st["w"].window
+    if "calls" not in st:              # arrays marshalled once: a step passes only its scalars
+        st["calls"] = [Z.AdamStep(inp["reps"], min(S, a + (W or S)) - a, inp["master"][a:],
+                                  inp["m"][a:], inp["v"][a:], out=st["slot"][a:])
+                       for a in range(0, S, W or S)]
     h = hparams(st)
-    if W is None:                      # one launch over the whole shard: no views to make
-        spans("k_adam_step", lambda: Z.zero_adam_shard_step(
-            inp["reps"], S, 1.0, inp["master"], inp["m"], inp["v"], h, out=st["slot"]))
-    else:
-        for a in range(0, S, W):
-            b = min(S, a + W)
-            spans("k_adam_step", lambda: Z.zero_adam_shard_step(
-                inp["reps"], b - a, 1.0, inp["master"][a:], inp["m"][a:], inp["v"][a:], h,
-                out=st["slot"][a:]))
+    for call in st["calls"]:
+        spans("k_adam_step", lambda: call(1.0, h))
     st["t"] += 1
 
 

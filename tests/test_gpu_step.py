@@ -440,3 +440,27 @@ def test_reduce_and_sqnorm_over_the_full_range():
         assert abs(sq.item() - want) <= 1e-10 * want
     else:
         assert math.isinf(sq.item()) or math.isnan(sq.item())
+
+
+def test_prepared_step_equals_the_plain_call():
+    """AdamStep (arrays marshalled once) gives the bits zero_adam_shard_step gives, step after step."""
+    n = 5 * TILE + 77
+    rng = np.random.default_rng(44)
+    reps = _reps_np(rng, 3, n, "bf16")
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    runs = []
+    for prepared in (False, True):
+        d_r = [dev_rep(r, "bf16") for r in reps]
+        d_p, d_m, d_v = dev_f32(master), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+        d_o = empty16(n, "bf16")
+        call = Z.AdamStep(d_r, n, d_p, d_m, d_v, out=d_o) if prepared else None
+        for t, gs in ((1, 1.0), (2, 0.5)):
+            hp = Z.adam_hparams(lr=1e-3, weight_decay=0.01, step=t)
+            if prepared:
+                call(gs, hp)
+            else:
+                Z.zero_adam_shard_step(d_r, n, gs, d_p, d_m, d_v, hp, out=d_o)
+        torch.cuda.synchronize()
+        runs.append((bits32(d_p), bits32(d_m), bits32(d_v), bits16(d_o)))
+    for a, b, what in zip(runs[0], runs[1], ("master", "m", "v", "out")):
+        assert_bits_equal(b, a, what)

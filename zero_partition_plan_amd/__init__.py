@@ -24,6 +24,7 @@ __all__ = [
     "zero_adam_derive", "ZeroArenaArray", "zero_arena_layout", "zero_arena_alloc", "zero_arena_free",
     "arena",
     "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
+    "AdamStep",
     "zero_gather_params", "zero_host_adam_step", "zero_offload_step",
     "zero_status_str", "zero_last_error",
 ]
@@ -328,6 +329,31 @@ def zero_adam_shard_step(reps, n: int, grad_scale: float, master, m, v, hp: Zero
         _ptr(m, n, "m", f32), _ptr(v, n, "v", f32), ctypes.byref(hp),
         _ptr(out, n, "out"), out_dt, _ptr(skip, 1, "skip", (torch.int32,)), _stream(stream)),
         "zero_adam_shard_step")
+
+
+class AdamStep:
+    """zero_adam_shard_step with its arrays and stream marshalled once; a call passes only the grad
+    scale and the hyper-parameters (which change every step). For loops whose steps are short enough
+    that per-call marshalling shows. The tensors must stay alive and in place while it is used."""
+
+    def __init__(self, reps, n: int, master, m, v, out=None, skip=None, stream=None):
+        self._src, self._keep = _src(reps, n)
+        f32 = (torch.float32,)
+        out_dt = ZERO_F32
+        if out is not None:
+            if out.dtype not in (torch.bfloat16, torch.float16):
+                raise TypeError("out must be bfloat16 or float16")
+            out_dt = _TORCH_DT[out.dtype]
+        self._tensors = (reps, master, m, v, out, skip)
+        self._fn = lib().zero_adam_shard_step
+        self._args = (n, _ptr(master, n, "master", f32), _ptr(m, n, "m", f32), _ptr(v, n, "v", f32))
+        self._tail = (_ptr(out, n, "out"), out_dt, _ptr(skip, 1, "skip", (torch.int32,)), _stream(stream))
+        self._ref = ctypes.byref(self._src)
+
+    def __call__(self, grad_scale: float, hp: ZeroAdamHParams):
+        n, p, m, v = self._args
+        _check(self._fn(self._ref, n, grad_scale, p, m, v, ctypes.byref(hp), *self._tail),
+               "zero_adam_shard_step")
 
 
 def zero_gather_params(shards, begin: int, count: int, out, stream=None):

@@ -12,6 +12,7 @@ Prints one JSON line (see the fields below). Flags:
   --gpus N         only 1 is supported: this path runs on one GPU's shard
   --steps K        timed steps (default 20)
   --warmup W       untimed steps first (default 3)
+  --config C       the same by config number: 2 gpt2, 3 llama7b, 4 llama13b, 5 gpt3
   --workload NAME  llama7b (default), gpt2, llama13b (two-pass clip path), gpt3 (64 Mi windows),
                    gather7b (ZeRO-3: every Llama-7B layer gathered from its 8 rank shards),
                    offload7b (ZeRO-Offload: the 7B shard's Adam state in host memory)
@@ -732,6 +733,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "gpt2", "llama13b", "llama13b-clean", "gpt3", "gather7b",
                              "offload7b"])
+    ap.add_argument("--config", type=int, choices=[2, 3, 4, 5],
+                    help="the workload by its config number: 2 gpt2, 3 llama7b, 4 llama13b, 5 gpt3 "
+                         "(config 1, the tiny all-ranks case, is a correctness case for the tests)")
     ap.add_argument("--placement", default="arena", choices=["arena", "separate"],
                     help="arrays of the step in one arena laid out by zero_arena_layout, or each in "
                          "its own allocation")
@@ -743,6 +747,8 @@ def main(argv=None):
     ap.add_argument("--summarize", action="store_true")
     ap.add_argument("--profile-commands", action="store_true")
     args = ap.parse_args(argv)
+    if args.config is not None:
+        args.workload = {2: "gpt2", 3: "llama7b", 4: "llama13b", 5: "gpt3"}[args.config]
     if args.profile_commands:
         for k, c in profile_commands(args.workload).items():
             print(f"{c} > {profile_dirs(args.workload)[k]}.log 2>&1")

@@ -70,3 +70,48 @@ def test_arena_alloc_edges():
     Z.zero_arena_free(p)
     with pytest.raises(Z.ZeroError):
         Z.zero_arena_alloc(1 << 62)                    # more than any device holds
+
+
+@pytest.mark.parametrize("nd", [3, 8])
+def test_step_on_arena_views_with_slot_offsets(nd):
+    """Every rank of a ragged plan steps on arena views, its slot found inside the gathered buffer
+    at r*S (the layout's hot offset): the slot equals the oracle's cast, bit for bit, and the rest
+    of the buffer is untouched."""
+    import numpy as np
+
+    import oracle as O
+    from gpu_util import assert_bits_equal, bits16, bits32, f32_bits
+
+    n = 1_234_567
+    plan = Z.zero_partition_plan(n, nd)
+    S = plan.shard_elems
+    rng = np.random.default_rng(nd)
+    for r in range(nd):
+        begin, valid = Z.zero_shard_range(plan, r)
+        specs = [(f"rep{k}", S, torch.bfloat16, 0, 0) for k in range(2)]
+        specs += [("full", plan.padded_n, torch.bfloat16, 0, begin), ("master", S, torch.float32, 1, 0),
+                  ("m", S, torch.float32, 1, 0), ("v", S, torch.float32, 1, 0)]
+        storage, a = Z.arena(specs, device=DEV)
+        reps = (rng.standard_normal((2, S)).astype(np.float32) * np.float32(1e-3)).view(np.uint32) >> 16
+        reps = reps.astype(np.uint16)
+        reps[:, valid:] = 0
+        master = (rng.standard_normal(S) * 0.02).astype(np.float32)
+        master[valid:] = 0
+        for k in range(2):
+            a[f"rep{k}"].copy_(torch.from_numpy(reps[k].view(np.int16)).view(torch.bfloat16))
+        a["master"].copy_(torch.from_numpy(master))
+        a["m"].zero_()
+        a["v"].zero_()
+        a["full"].fill_(-9.0)
+        hp = dict(lr=1e-3, weight_decay=0.01, step=1)
+        Z.zero_adam_shard_step([a["rep0"], a["rep1"]], S, 1.0, a["master"], a["m"], a["v"],
+                               Z.adam_hparams(**hp), out=a["full"][begin:begin + S])
+        torch.cuda.synchronize()
+        z = np.zeros(S, np.float32)
+        wp, _, _, wo = O.sharded_step(list(reps), "bf16", 1.0, master, z, z, O.AdamHParams(**hp), "bf16")
+        assert_bits_equal(bits32(a["master"]), f32_bits(wp), f"master r={r}")
+        full = bits16(a["full"])
+        assert_bits_equal(full[begin:begin + S], wo, f"slot r={r}")
+        fill = O.cast_bf16_rne(np.float32([-9.0]))[0]
+        assert (full[:begin] == fill).all() and (full[begin + S:] == fill).all(), f"outside r={r}"
+        del storage, a

@@ -87,3 +87,44 @@ def test_offload_rejects_bad_buffers():
         Z.zero_offload_step([d_rep], n, 1.0, *h, Z.adam_hparams(), slot, bufs)
     with pytest.raises(Z.ZeroError):                  # host state aliasing
         Z.zero_offload_step([d_rep], n, 1.0, h[0], h[0], h[2], Z.adam_hparams(), slot, Z.offload_buffers(64))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_offload_random_configurations(seed):
+    """Seeded random sizes, chunk sizes (also larger than the shard), host thread counts, replica
+    counts and dtypes, output dtypes, decay modes and copy-back streams, against the oracle."""
+    rng = np.random.default_rng(40_000 + seed)
+    n = int(rng.choice([rng.integers(1, 2000), rng.integers(2000, 300_000)]))
+    chunk = int(rng.choice([1, 7, 256, 4096, 65536, 1 << 20]))
+    threads = int(rng.choice([0, 1, 3, 8]))
+    R = int(rng.choice([1, 2, 5, 8, 16]))
+    rdt = str(rng.choice(["f32", "f16", "bf16"]))
+    odt = str(rng.choice(["bf16", "f16"]))
+    mode = str(rng.choice(["adamw", "l2"]))
+    side = bool(rng.integers(0, 2))
+    banner(f"offload random seed={seed} n={n} chunk={chunk} threads={threads} R={R} {rdt}->{odt} {mode}")
+    x = rng.standard_normal((R, n)).astype(np.float32) * np.float32(1e-3)
+    if rdt == "f32":
+        reps = x
+    elif rdt == "bf16":
+        reps = (x.view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        reps = (x * np.float32(64)).astype(np.float16).view(np.uint16)
+    d_reps = [dev_rep(r, rdt) for r in reps]
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (rng.random(n) * 1e-7).astype(np.float32)
+    kw = {**HP, "wd_mode": mode, "step": int(rng.integers(1, 100))}
+    hm, hmm, hv = master.copy(), m.copy(), v.copy()
+    t16 = torch.bfloat16 if odt == "bf16" else torch.float16
+    slot = torch.full((n + 6,), -1.0, dtype=t16, device=DEV)
+    bufs = Z.offload_buffers(chunk, threads=threads, h2d_stream=torch.cuda.Stream() if side else None)
+    Z.zero_offload_step(d_reps, n, 0.25, hm, hmm, hv, Z.adam_hparams(**kw), slot[3:3 + n], bufs)
+    torch.cuda.synchronize()
+    p2, m2, v2, o2 = O.sharded_step(list(reps), rdt, 0.25, master, m, v, O.AdamHParams(**kw), odt)
+    assert_bits_equal(hm.view(np.uint32), f32_bits(p2), "host master")
+    assert_bits_equal(hmm.view(np.uint32), f32_bits(m2), "host m")
+    assert_bits_equal(hv.view(np.uint32), f32_bits(v2), "host v")
+    got = bits16(slot)
+    assert (got[:3] == got[0]).all() and (got[3 + n:] == got[0]).all(), "write outside the slot"
+    assert_bits_equal(got[3:3 + n], o2, "slot")

@@ -727,9 +727,9 @@ def cpu_baseline(name: str, seconds: float):
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description="sharded ZeRO AdamW step benchmark")
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--gpus", type=int, default=1, help="GPUs (only 1: one rank's shard on one GPU)")
+    ap.add_argument("--steps", type=int, default=20, help="timed steps")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed steps first")
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "gpt2", "llama13b", "llama13b-clean", "gpt3", "gather7b",
                              "offload7b"])
@@ -742,10 +742,14 @@ def main(argv=None):
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context legs (copy ceiling, separate-placement step, cold launches), "
                          "so that a profiler sees only the timed step's launches")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--copy-calib", type=int, default=0)
-    ap.add_argument("--summarize", action="store_true")
-    ap.add_argument("--profile-commands", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the oracle's CPU baseline (0 skips it)")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize", action="store_true",
+                    help="(no GPU) write the profile summaries under profiles/ from the profile runs")
+    ap.add_argument("--profile-commands", action="store_true",
+                    help="print the profiling commands for --workload and exit")
     args = ap.parse_args(argv)
     if args.config is not None:
         args.workload = {2: "gpt2", 3: "llama7b", 4: "llama13b", 5: "gpt3"}[args.config]

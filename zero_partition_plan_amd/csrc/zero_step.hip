@@ -344,16 +344,23 @@ __device__ __forceinline__ void reduce_tile(const RepPtrs& reps, int nrep, uint6
   }
 }
 
-// whole, aligned tiles with vector loads
-template <int RDT, int RFIX>
+// whole, aligned tiles with vector loads; with TAIL the grid has one block more, which takes the
+// partial last tile element by element (same element order, so its partial is the same)
+template <int RDT, int RFIX, bool TAIL>
 __global__ __launch_bounds__(64) void k_reduce(RepPtrs reps, int nrep, uint64_t first_tile,
                                                uint64_t n, float* __restrict__ G,
                                                int32_t* __restrict__ flag,
                                                double* __restrict__ partials, double sq_scale) {
+  if constexpr (TAIL) {
+    if (blockIdx.x == gridDim.x - 1) {
+      reduce_tile<RDT, 0, false>(reps, nrep, first_tile + blockIdx.x, n, G, flag, partials, sq_scale);
+      return;
+    }
+  }
   reduce_tile<RDT, RFIX, true>(reps, nrep, first_tile + blockIdx.x, n, G, flag, partials, sq_scale);
 }
 
-// the ragged last tile, or every tile of arrays that are not aligned: element by element
+// every tile of arrays that are not aligned: element by element
 template <int RDT>
 __global__ __launch_bounds__(64) void k_reduce_tail(RepPtrs reps, int nrep, uint64_t first_tile,
                                                     uint64_t n, float* __restrict__ G,
@@ -534,30 +541,50 @@ struct ReduceArgs {
 };
 
 // tiles [t0, t1) in grids of at most kMaxGrid blocks
-template <int RDT, int RFIX, bool VEC>
-void launch_reduce(const ReduceArgs& a, uint64_t t0, uint64_t t1) {
-  for (uint64_t t = t0; t < t1; t += kMaxGrid) {
-    const uint64_t g = t1 - t < kMaxGrid ? t1 - t : kMaxGrid;
-    if constexpr (VEC)
-      hipLaunchKernelGGL((k_reduce<RDT, RFIX>), dim3((unsigned)g), dim3(64), 0, a.stream, a.reps,
-                         a.nrep, t, a.n, a.G, a.flag, a.partials, a.sq_scale);
-    else
-      hipLaunchKernelGGL((k_reduce_tail<RDT>), dim3((unsigned)g), dim3(64), 0, a.stream, a.reps,
-                         a.nrep, t, a.n, a.G, a.flag, a.partials, a.sq_scale);
+// aligned arrays: tiles [0, full) as vector tiles in grids of at most kMaxGrid blocks; a partial
+// last tile rides on the last grid as one extra block (a shard shorter than one tile is a grid of
+// that block alone)
+template <int RDT, int RFIX>
+void launch_reduce_vec(const ReduceArgs& a, uint64_t full, bool tail) {
+  uint64_t t = 0;
+  do {
+    const uint64_t g = full - t < kMaxGrid ? full - t : kMaxGrid;
+    if (tail && t + g == full)
+      hipLaunchKernelGGL((k_reduce<RDT, RFIX, true>), dim3((unsigned)(g + 1)), dim3(64), 0,
+                         a.stream, a.reps, a.nrep, t, a.n, a.G, a.flag, a.partials, a.sq_scale);
+    else if (g > 0)
+      hipLaunchKernelGGL((k_reduce<RDT, RFIX, false>), dim3((unsigned)g), dim3(64), 0, a.stream,
+                         a.reps, a.nrep, t, a.n, a.G, a.flag, a.partials, a.sq_scale);
+    t += g;
+  } while (t < full);
+}
+
+// arrays that are not aligned: every tile element by element, in grids of at most kMaxGrid
+template <int RDT>
+void launch_reduce_elem(const ReduceArgs& a, uint64_t tiles) {
+  for (uint64_t t = 0; t < tiles; t += kMaxGrid) {
+    const uint64_t g = tiles - t < kMaxGrid ? tiles - t : kMaxGrid;
+    hipLaunchKernelGGL((k_reduce_tail<RDT>), dim3((unsigned)g), dim3(64), 0, a.stream, a.reps,
+                       a.nrep, t, a.n, a.G, a.flag, a.partials, a.sq_scale);
   }
 }
 
 template <int RDT>
 void reduce_kernels(const ReduceArgs& a, bool vec) {
-  const uint64_t all = red_tiles(a.n), full = vec ? a.n / kRedTile : 0;
-  switch (a.nrep) {
-    case 1: launch_reduce<RDT, 1, true>(a, 0, full); break;
-    case 8: launch_reduce<RDT, 8, true>(a, 0, full); break;
-    case 16: launch_reduce<RDT, 16, true>(a, 0, full); break;
-    case 64: launch_reduce<RDT, 64, true>(a, 0, full); break;
-    default: launch_reduce<RDT, 0, true>(a, 0, full); break;
+  const uint64_t all = red_tiles(a.n);
+  if (!vec) {
+    launch_reduce_elem<RDT>(a, all);
+    return;
   }
-  launch_reduce<RDT, 0, false>(a, full, all);  // ragged last tile, or every tile if unaligned
+  const uint64_t full = a.n / kRedTile;
+  const bool tail = all > full;
+  switch (a.nrep) {
+    case 1: launch_reduce_vec<RDT, 1>(a, full, tail); break;
+    case 8: launch_reduce_vec<RDT, 8>(a, full, tail); break;
+    case 16: launch_reduce_vec<RDT, 16>(a, full, tail); break;
+    case 64: launch_reduce_vec<RDT, 64>(a, full, tail); break;
+    default: launch_reduce_vec<RDT, 0>(a, full, tail); break;
+  }
 }
 
 zero_status reduce_impl(const zero_grad_src* src, uint64_t n, float* G, int32_t* flag,

@@ -133,9 +133,11 @@ zero_status zero_choose_stage(const zero_plan* p, uint64_t usable_bytes, uint32_
  * arrays[i]: bytes (the array's size), hot_offset (byte offset inside the array where the kernel's
  * walk starts, e.g. r*S*2 for rank r's slot inside a gathered 16-bit buffer; else 0), group (arrays
  * a kernel reads or writes at the same element index share a group id; ids are arbitrary) and
- * elem_bytes (2 or 4). Arrays are placed in the given order, each after the previous one ends; the
- * k-th member of a group (counted in that order) gets its hot start at a multiple of
- * ZERO_ARENA_GRANULE plus k * ZERO_ARENA_STAGGER16 (16-bit) or k * ZERO_ARENA_STAGGER32 (fp32).
+ * elem_bytes (2 or 4). Arrays are placed in the given order, each after the previous one ends. An
+ * array's granule is its byte size rounded up to a power of two, at least ZERO_ARENA_MIN_GRANULE and
+ * at most ZERO_ARENA_GRANULE; the k-th member of a group (counted in that order) gets its hot start
+ * at a multiple of its granule plus k * ZERO_ARENA_STAGGER16 (16-bit) or k * ZERO_ARENA_STAGGER32
+ * (fp32), modulo the granule.
  * offsets[i] (host, count entries) receives array i's byte offset from the arena start and
  * *total_bytes the size to allocate. Only offsets relative to one allocation matter: any
  * 256-byte-aligned allocation of total_bytes works, and every hot start is then 2 KiB aligned.
@@ -144,6 +146,7 @@ zero_status zero_choose_stage(const zero_plan* p, uint64_t usable_bytes, uint32_
  * ZERO_E_OVERFLOW. */
 #define ZERO_ARENA_MAX_ARRAYS 256
 #define ZERO_ARENA_GRANULE (256ull << 20)
+#define ZERO_ARENA_MIN_GRANULE (4ull << 20)
 #define ZERO_ARENA_STAGGER16 2048ull
 #define ZERO_ARENA_STAGGER32 12288ull
 typedef struct {

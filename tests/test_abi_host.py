@@ -205,12 +205,22 @@ def test_status_strings():
 
 
 Q = 256 << 20                                   # ZERO_ARENA_GRANULE
+QMIN = 4 << 20                                  # ZERO_ARENA_MIN_GRANULE
 STAGGER = {2: 2048, 4: 12288}                   # ZERO_ARENA_STAGGER16 / 32
+
+
+def granule(nbytes):
+    """An array's line: its size rounded up to a power of two, within [QMIN, Q]."""
+    q = QMIN
+    while q < nbytes and q < Q:
+        q *= 2
+    return q
 
 
 def test_arena_constants_match_header():
     text = open(HEADER).read()
     assert re.search(r"#define ZERO_ARENA_GRANULE \(256ull << 20\)", text)
+    assert re.search(r"#define ZERO_ARENA_MIN_GRANULE \(4ull << 20\)", text)
     assert int(re.search(r"#define ZERO_ARENA_STAGGER16 (\d+)ull", text).group(1)) == STAGGER[2]
     assert int(re.search(r"#define ZERO_ARENA_STAGGER32 (\d+)ull", text).group(1)) == STAGGER[4]
     assert ctypes.sizeof(Z.ZeroArenaArray) == 24
@@ -221,8 +231,9 @@ def _check_layout(arrays, offs, total):
     for (nbytes, hot, group, eb), off in zip(arrays, offs):
         k = member.get(group, 0)
         member[group] = k + 1
-        assert off >= end and off - end < Q                  # in order, no overlap, gap < granule
-        assert (off + hot) % Q == (k * STAGGER[eb]) % Q      # hot start: granule + k * stagger
+        q = granule(nbytes)
+        assert off >= end and off - end < q                  # in order, no overlap, gap < granule
+        assert (off + hot) % q == (k * STAGGER[eb]) % q      # hot start: granule line + k * stagger
         assert off % eb == 0 and (off + hot) % 2048 == 0
         end = off + nbytes
     assert total == end

@@ -67,14 +67,15 @@ arrays = st.lists(st.tuples(st.integers(0, 1 << 34), st.floats(0, 1), st.integer
 @SETTINGS
 @given(arrays=arrays)
 def test_arena_layout_invariants(arrays):
-    Q, stagger = 256 << 20, {2: 2048, 4: 12288}
+    stagger = {2: 2048, 4: 12288}
     spec = [(n * eb, int(n * f) * eb, g, eb) for n, f, g, eb in arrays]
     offs, total = Z.zero_arena_layout(spec)
     member, end = {}, 0
     for (nbytes, hot, g, eb), off in zip(spec, offs):
         k = member.get(g, 0)
         member[g] = k + 1
-        assert end <= off < end + Q
-        assert (off + hot) % Q == (k * stagger[eb]) % Q
+        q = 1 << max(22, min(28, (max(nbytes, 1) - 1).bit_length()))   # [4 MiB, 256 MiB]
+        assert end <= off < end + q
+        assert (off + hot) % q == (k * stagger[eb]) % q
         end = off + nbytes
     assert total == end

@@ -123,16 +123,16 @@ zero_status zero_choose_stage(const zero_plan* p, uint64_t usable_bytes, uint32_
 // Placement of one pass's arrays in a single allocation. Not from the pages: a property of this
 // GPU's memory system. Arrays that a kernel walks at the same element index ("lockstep") hit the same
 // DRAM channels and banks when their starts agree in the address bits the interleave hashes; the
-// fused step then loses up to 5% of its bandwidth. Here every hot start sits a multiple of 256 MiB
-// past the arena start plus a stagger of k * 2 KiB (16-bit arrays) or k * 12 KiB (fp32 arrays) for
-// the k-th member of its lockstep group, the spacing that measured best on the step's kernels.
+// fused step then loses up to 5% of its bandwidth. Here every hot start sits on a line of the
+// array's granule (its size rounded up to a power of two, from 4 MiB to 256 MiB) past the arena
+// start, plus a stagger of k * 2 KiB (16-bit arrays) or k * 12 KiB (fp32 arrays) for the k-th member
+// of its lockstep group: the spacing that measured best on the step's kernels.
 zero_status zero_arena_layout(const zero_arena_array* arrays, uint32_t count, uint64_t* offsets,
                               uint64_t* total_bytes) {
   const char* fn = "zero_arena_layout";
   if (!arrays || !offsets || !total_bytes) return fail(ZERO_E_INVAL, "%s: NULL argument", fn);
   if (count == 0 || count > ZERO_ARENA_MAX_ARRAYS)
     return fail(ZERO_E_INVAL, "%s: count %u outside 1..%d", fn, count, ZERO_ARENA_MAX_ARRAYS);
-  const uint64_t Q = ZERO_ARENA_GRANULE;
   uint32_t seen_group[ZERO_ARENA_MAX_ARRAYS], seen_count[ZERO_ARENA_MAX_ARRAYS];
   uint32_t ngroups = 0;
   uint64_t cursor = 0;
@@ -151,6 +151,8 @@ zero_status zero_arena_layout(const zero_arena_array* arrays, uint32_t count, ui
       ++ngroups;
     }
     const uint64_t member = seen_count[g]++;
+    uint64_t Q = ZERO_ARENA_MIN_GRANULE;      // the array's granule
+    while (Q < a.bytes && Q < ZERO_ARENA_GRANULE) Q <<= 1;
     const uint64_t stagger = a.elem_bytes == 2 ? ZERO_ARENA_STAGGER16 : ZERO_ARENA_STAGGER32;
     const uint64_t delta = (member * stagger) % Q;
     // smallest base >= cursor with base + hot_offset == delta (mod Q)

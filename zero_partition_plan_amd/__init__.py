@@ -249,7 +249,8 @@ def arena(specs, device="cuda", contiguous: bool = True):
         with torch.cuda.device(dev):
             mem = _ArenaMemory(max(total, 1))
             storage = torch.as_tensor(mem, device=dev)
-        assert storage.data_ptr() == mem.ptr and storage.numel() == max(total, 1)
+        if storage.data_ptr() != mem.ptr or storage.numel() != max(total, 1):
+            raise RuntimeError("torch did not wrap the arena allocation in place")
         storage.zero_arena_contiguous = mem.contiguous
     else:
         storage = torch.empty(max(total, 1), dtype=torch.uint8, device=dev)

@@ -27,7 +27,8 @@ def _new(empty, name: str, size: int, dtype, device) -> torch.Tensor:
     if empty is None:
         return torch.empty(size, dtype=dtype, device=device)
     t = empty(name, size, dtype)
-    assert t.shape == (size,) and t.dtype == dtype, (name, t.shape, t.dtype)
+    if t.shape != (size,) or t.dtype != dtype:
+        raise ValueError(f"storage for {name}: got {tuple(t.shape)} {t.dtype}, need ({size},) {dtype}")
     return t
 
 

@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <utility>
 
 #include "zero_device.h"
@@ -395,21 +396,25 @@ __global__ __launch_bounds__(kBlock) void k_sq_finalize(const double* __restrict
 // host side
 
 constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices];  // per-device compute-unit count, filled on first use
+// per-device compute-unit count, filled on first use; threads that fill it at once store the same
+// value, and the atomics make that well defined
+std::atomic<int> g_cu_count[kMaxDevices];
 
 zero_status cu_count(int* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return zero::fail(ZERO_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
   if (dev < 0 || dev >= kMaxDevices) return zero::fail(ZERO_E_UNSUPPORTED, "device index %d", dev);
-  if (g_cu_count[dev] == 0) {
+  int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (cached == 0) {
     int cus = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess)
       return zero::fail(ZERO_E_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
-    g_cu_count[dev] = cus > 0 ? cus : 1;
+    cached = cus > 0 ? cus : 1;
+    g_cu_count[dev].store(cached, std::memory_order_relaxed);
   }
-  *out = g_cu_count[dev];
+  *out = cached;
   return ZERO_OK;
 }
 

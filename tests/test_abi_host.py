@@ -304,3 +304,34 @@ def test_arena_views_on_host_memory():
         views[name].fill_(float(i + 1))
     for i, (name, *_rest) in enumerate(specs):
         assert (views[name] == float(i + 1)).all(), name
+
+
+def test_error_messages_are_per_thread():
+    """zero_last_error() is thread-local: threads that fail in different ways at the same time each
+    read their own message (ctypes releases the GIL for the call, so the calls overlap)."""
+    import threading
+
+    L = Z.lib()
+    results, start = {}, threading.Barrier(8)
+
+    def worker(k):
+        plan = Z.ZeroPlan()
+        start.wait()
+        seen = set()
+        for _ in range(2000):
+            if k % 2:
+                assert L.zero_partition_plan(5, 0, 1, ctypes.byref(plan)) == 1
+                want = "nd must be >= 1"
+            else:
+                assert L.zero_partition_plan(5, 1, 0, ctypes.byref(plan)) == 1
+                want = "align_elems must be >= 1"
+            msg = L.zero_last_error().decode()
+            seen.add(want in msg)
+        results[k] = seen
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert all(v == {True} for v in results.values()), results

@@ -464,3 +464,49 @@ def test_prepared_step_equals_the_plain_call():
         runs.append((bits32(d_p), bits32(d_m), bits32(d_v), bits16(d_o)))
     for a, b, what in zip(runs[0], runs[1], ("master", "m", "v", "out")):
         assert_bits_equal(b, a, what)
+
+
+def test_concurrent_steps_from_host_threads():
+    """Six host threads, each with its own stream and arrays, step at the same time: every result
+    equals the oracle's bit for bit (launch setup, the CU-count cache and error state are safe to use
+    from several threads)."""
+    import threading
+
+    n = 7 * TILE + 333
+    jobs = []
+    for k in range(6):
+        rng = np.random.default_rng(500 + k)
+        reps = _reps_np(rng, 1 + k, n, ["bf16", "f16", "f32"][k % 3])
+        master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        jobs.append((reps, ["bf16", "f16", "f32"][k % 3], master))
+    hp = {k: v for k, v in HP.items() if k != "step"}
+    out = [None] * len(jobs)
+    barrier = threading.Barrier(len(jobs), timeout=60)
+
+    def work(k):
+        reps, dt, master = jobs[k]
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            d_r = [dev_rep(r, dt) for r in reps]
+            d_p = dev_f32(master)
+            d_m, d_v = torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+            d_o = empty16(n, "bf16")
+            s.synchronize()
+            barrier.wait()
+            for t in (1, 2, 3):
+                Z.zero_adam_shard_step(d_r, n, 1.0, d_p, d_m, d_v, Z.adam_hparams(step=t, **hp), out=d_o)
+            s.synchronize()
+        out[k] = (bits32(d_p), bits16(d_o))
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(len(jobs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for k, (reps, dt, master) in enumerate(jobs):
+        p, m, v = master, np.zeros(n, np.float32), np.zeros(n, np.float32)
+        for t in (1, 2, 3):
+            p, m, v, o = O.sharded_step(list(reps), dt, 1.0, p, m, v, O.AdamHParams(step=t, **hp), "bf16")
+        assert out[k] is not None, f"thread {k} did not finish"
+        assert_bits_equal(out[k][0], f32_bits(p), f"master, thread {k}")
+        assert_bits_equal(out[k][1], o, f"out, thread {k}")

@@ -84,12 +84,38 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def code_only(text: str) -> str:
+    """C/C++ source with its comments removed and every run of whitespace made one space; string
+    and character literals are kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_hash(kernel: str) -> str:
-    """sha256[:16] over the device sources of ``kernel``: a counter summary is used only for the
-    exact code it was taken on."""
+    """sha256[:16] over the code (comments and layout left out) of the device sources of
+    ``kernel``: a counter summary is used only for the exact code it was taken on."""
     h = hashlib.sha256()
     for f in KERNEL_SRCS[kernel]:
-        h.update(open(f, "rb").read())
+        h.update(code_only(open(f).read()).encode())
     return h.hexdigest()[:16]
 
 

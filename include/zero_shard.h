@@ -180,7 +180,7 @@ zero_status zero_arena_free(void* d_ptr);
 zero_status zero_adam_derive(const zero_adam_hparams* hp, zero_adam_scalars* out);
 
 /* Length, in doubles, of the squared-norm partials buffer for a shard of n elements:
- * ceil(n / 512) per-tile partials followed by 1024 second-level slots. Host only; never fails. */
+ * ceil(n / 256) per-tile partials followed by 1024 second-level slots. Host only; never fails. */
 uint64_t zero_sq_partials_len(uint64_t n);
 
 /* Reduction half of the gradient reduce-scatter, done over local replicas (P1 section 二; P2 ZeRO
@@ -189,8 +189,8 @@ uint64_t zero_sq_partials_len(uint64_t n);
  *   out_grad      device float[n]: acc.
  *   d_nonfinite   device int32: set to 1 if any acc[i] is +-inf or NaN, otherwise left as is
  *                 (so several calls OR into it; the caller zeroes it first).
- *   d_sq_partials device double[zero_sq_partials_len(n)]: entry t (t < ceil(n/512)) receives
- *                 sum over i in [512t, 512t+512) of (double(acc[i]) * sq_scale)^2, each in a fixed
+ *   d_sq_partials device double[zero_sq_partials_len(n)]: entry t (t < ceil(n/256)) receives
+ *                 sum over i in [256t, 256t+256) of (double(acc[i]) * sq_scale)^2, each in a fixed
  *                 order that does not depend on alignment; finish with zero_shard_sqnorm(NULL, n).
  * n == 0 enqueues nothing. Aliasing: out_grad and d_sq_partials must not overlap a replica or each
  * other. Errors: bad source, no output, aliasing -> ZERO_E_INVAL; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */

@@ -176,9 +176,9 @@ def test_device_entry_points_validate_first():
 
 
 def test_sq_partials_len():
-    # one partial per 512-element tile, then 1024 second-level slots
-    for n, want in ((0, 1024), (1, 1025), (512, 1025), (513, 1026), (813_491_520, 1_588_851 + 1024),
-                    (1 << 40, (1 << 31) + 1024)):
+    # one partial per 256-element tile, then 1024 second-level slots; no wrap-around at the top
+    for n, want in ((0, 1024), (1, 1025), (256, 1025), (257, 1026), (813_491_520, 3_177_702 + 1024),
+                    (1 << 40, (1 << 32) + 1024), ((1 << 64) - 1, (1 << 56) + 1024)):
         assert Z.zero_sq_partials_len(n) == want, n
 
 

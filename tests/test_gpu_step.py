@@ -19,7 +19,7 @@ from workloads.extremes import EXTREME_CASES, f16_all_patterns, f32_patterns, mi
 
 pytestmark = pytest.mark.gpu
 
-TILE = 512  # elements per reduce-kernel tile (64 threads x 4 x 2); two Adam-kernel tiles of 256
+TILE = 256  # elements per tile of both the reduce and the Adam kernel (64 threads x 4)
 
 
 def _reps_np(rng, R, n, dtype, std=1e-3, valid=None):
@@ -254,7 +254,7 @@ def test_reduce_sizes_and_misalignment(n):
 
 
 def test_reduce_per_tile_partials():
-    """Partial t is the squared norm of tile t alone (elements [512t, 512t + 512))."""
+    """Partial t is the squared norm of tile t alone (elements [256t, 256t + 256))."""
     n = 37 * TILE + 101
     rng = np.random.default_rng(77)
     reps = _reps_np(rng, 8, n, "f16")

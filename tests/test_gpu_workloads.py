@@ -5,7 +5,7 @@ step runs on the whole shard, and the same windows of the outputs are compared w
 run on the downloaded inputs: bit for bit for fp32 state and 16-bit parameters. The 7B, 13B and
 GPT-3 shards sit in one arena placed by zero_arena_layout, as the benchmark places them; the GPT-2
 shard uses separate allocations. For the squared
-norm, sampled tiles' fp64 partial sums (one per 512-element tile) are recomputed by the oracle from
+norm, sampled tiles' fp64 partial sums (one per 256-element tile) are recomputed by the oracle from
 downloaded replica tiles, and the total is checked against the partials."""
 
 import dataclasses
@@ -26,7 +26,7 @@ from workloads.placement import step_arrays
 pytestmark = pytest.mark.gpu
 
 WIN = 1 << 22                    # elements per checked window
-TILE = 512                       # reduce-kernel tile: one squared-norm partial each
+TILE = 256                       # reduce-kernel tile: one squared-norm partial each
 
 
 def _hp(w, step):

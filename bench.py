@@ -77,7 +77,7 @@ WL_DESC = {
 }
 GATHER_LAYERS = 34          # embeddings, 32 blocks, final norm + head
 OFFLOAD_CHUNK = 32 << 20    # elements per pipeline chunk
-OFFLOAD_THREADS = 16        # host threads (the machine's CPU share for one GPU)
+OFFLOAD_THREADS = 16        # host threads: a 16-core host share per GPU
 
 
 def log(msg):
@@ -725,7 +725,7 @@ def _oracle_worker(args):
 
 
 CPU_WINDOW = 1 << 21
-CPU_WORKERS = 16            # the machine's host-core share for one GPU
+CPU_WORKERS = 16            # host cores: a 16-core host share per GPU
 
 
 def cpu_baseline(name: str, seconds: float):
@@ -787,7 +787,7 @@ def main(argv=None):
         summarize(args.workload)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one rank's shard "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark measures one rank's shard "
               f"on one GPU (--gpus 1); a multi-GPU run would add the reduce-scatter and all-gather "
               f"around this step", file=sys.stderr, flush=True)
         return 2

@@ -77,7 +77,7 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
 
 // fp32 -> 16-bit, round to nearest even, two values packed low-then-high. bf16 uses gfx950's
 // v_cvt_pk_bf16_f32: checked against the integer rule (u + 0x7fff + ((u >> 16) & 1)) >> 16, with a
-// NaN becoming (u >> 16) | 0x40, on all 2^32 fp32 patterns in this build's floating-point mode.
+// NaN becoming (u >> 16) | 0x40, on all 2^32 fp32 patterns in the library's floating-point mode.
 // binary16 uses the IEEE conversion in the default rounding mode.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));

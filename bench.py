@@ -372,11 +372,13 @@ def setup(name: str, placement: str = "arena"):
     if two_pass:
         state["g"] = views["g"] if views else torch.empty(S, device=dev)
         state["flag"] = torch.zeros(1, dtype=torch.int32, device=dev)
-        state["host_sq"] = torch.zeros(1, dtype=torch.float64, pin_memory=True)
         state["host_flag"] = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+        state["flag_ready"] = torch.cuda.Event()
+        state["flag_pending"] = None       # Spans of the step whose flag the host has not read yet
         state["skipped"] = 0
         state["parts"] = torch.empty(Z.zero_sq_partials_len(S), dtype=torch.float64, device=dev)
         state["sq"] = torch.empty(1, dtype=torch.float64, device=dev)
+        state["gs"] = torch.empty(1, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     return state
 
@@ -637,6 +639,11 @@ class Spans:
     def ms(self, name):
         return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
 
+    def relabel_last(self, name, new_name):
+        """File the last span of ``name`` under ``new_name`` instead."""
+        if self.on and self.pairs.get(name):
+            self.pairs.setdefault(new_name, []).append(self.pairs[name].pop())
+
 
 def step_fused(st, spans):
     """One step of a fused workload: one launch per window (one window unless the shard is windowed)."""
@@ -653,33 +660,44 @@ def step_fused(st, spans):
 
 
 def step_two_pass(st, spans):
-    """Reduce -> squared norm -> one 12-byte read of (norm, flag) -> clip scale on the host -> AdamW.
+    """Reduce -> squared norm -> clip scale -> AdamW, all enqueued on the device with nothing read
+    back between the passes: zero_clip_scale forms the grad scale from the device norm, and the
+    update reads it and the overflow flag from device memory (a flagged step writes nothing).
 
-    The host already waits for the squared norm to form the clip coefficient, so it reads the
-    overflow flag in the same copy and does not launch the update when it is set (t does not
-    advance). The update still gets the device flag, as a caller that does not read it back would.
+    The host learns a step's flag one step late, from a 4-byte copy enqueued after its reduce pass:
+    the next step waits for that copy (the GPU meanwhile runs this step's update), and t advances
+    only past steps that were not skipped.
     """
-    import torch
-
     import zero_partition_plan_amd as Z
+    resolve_two_pass(st)
     w, inp, S = st["w"], st["inp"], st["S"]
     inv_ls = 1.0 / w.loss_scale
     st["flag"].zero_()
     spans("k_reduce", lambda: Z.zero_reduce_shard(inp["reps"], S, st["g"], st["flag"], st["parts"],
                                                   inv_ls))
-    Z.zero_shard_sqnorm(None, S, inv_ls, st["parts"], st["sq"])
-    st["host_sq"].copy_(st["sq"], non_blocking=True)
     st["host_flag"].copy_(st["flag"], non_blocking=True)
-    torch.cuda.current_stream().synchronize()
-    sq, flag = float(st["host_sq"][0]), int(st["host_flag"][0])
-    if flag:
-        st["skipped"] += 1
-        return
-    coef = min(1.0, w.max_norm / (math.sqrt(sq) + 1e-6))
-    spans("k_adam_step", lambda: Z.zero_adam_shard_step(
-        [st["g"]], S, coef * inv_ls, inp["master"], inp["m"], inp["v"], hparams(st), out=st["slot"],
+    st["flag_ready"].record()
+    Z.zero_shard_sqnorm(None, S, inv_ls, st["parts"], st["sq"])
+    Z.zero_clip_scale(st["sq"], w.max_norm, 1e-6, inv_ls, st["gs"])
+    spans("k_adam_step", lambda: Z.zero_adam_shard_step_dev_scale(
+        [st["g"]], S, st["gs"], inp["master"], inp["m"], inp["v"], hparams(st), out=st["slot"],
         skip=st["flag"]))
-    st["t"] += 1
+    st["flag_pending"] = spans
+
+
+def resolve_two_pass(st):
+    """Account for the last two-pass step once its flag is on the host: t advances unless it was
+    skipped; a skipped step's update launch (which exits at once) is timed apart from real ones."""
+    spans = st.get("flag_pending")
+    if spans is None:
+        return
+    st["flag_ready"].synchronize()
+    st["flag_pending"] = None
+    if int(st["host_flag"][0]):
+        st["skipped"] += 1
+        spans.relabel_last("k_adam_step", "k_adam_step_skipped")
+    else:
+        st["t"] += 1
 
 
 def new_event(record=False):
@@ -831,6 +849,8 @@ def main(argv=None):
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    if "flag_pending" in st:
+        resolve_two_pass(st)           # the last step's overflow flag
     nvtx.range_pop()
     gc.enable()
     total_ms = t_start.elapsed_time(t_end)
@@ -868,6 +888,10 @@ def main(argv=None):
             f"{per_kernel[k]['p90_ms']:.4f} -> {per_kernel[k]['gbs_at_avg']:.0f} GB/s")
     if "skipped" in st:
         log(f"overflow-skipped steps: {st['skipped']} of {args.warmup + args.steps}")
+        xs = spans.ms("k_adam_step_skipped")
+        if xs:
+            log(f"k_adam_step on a set skip flag (exits at once): {len(xs)} launches, avg "
+                f"{sum(xs) / len(xs):.4f} ms")
     log(f"{args.steps} steps: {total_ms:.3f} ms on events, {wall * 1e3:.3f} ms wall")
     if "inp" in st:
         assert torch.isfinite(st["inp"]["master"][:1 << 20]).all()

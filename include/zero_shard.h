@@ -232,6 +232,31 @@ zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float gra
                                  void* out_param, int32_t out_dtype, const int32_t* d_skip,
                                  void* stream);
 
+/* The same step with its grad scale read from device memory: *d_grad_scale (device float) is read
+ * once per launch in place of a host grad_scale, as zero_clip_scale writes it. With it the
+ * two-pass step (zero_reduce_shard, zero_shard_sqnorm, zero_clip_scale, this call) is enqueued
+ * with nothing read back to the host between its passes, and can be captured in a graph.
+ * Everything else is as zero_adam_shard_step. Errors: as zero_adam_shard_step, plus d_grad_scale
+ * NULL or overlapping master, m, v or out_param -> ZERO_E_INVAL. */
+zero_status zero_adam_shard_step_dev_scale(const zero_grad_src* src, uint64_t n,
+                                           const float* d_grad_scale, float* master, float* m,
+                                           float* v, const zero_adam_hparams* hp, void* out_param,
+                                           int32_t out_dtype, const int32_t* d_skip, void* stream);
+
+/* Gradient-clipping scale for the two-pass step, formed on the device. The pages do not clip; this
+ * is the usual global-norm rule, with the shard's squared norm standing for the global one:
+ *   q = max_norm / (sqrt(*d_sq) + clip_eps)       fp64, each operation correctly rounded
+ *   coef = q < 1 ? q : 1                           (a NaN q gives 1)
+ *   *d_grad_scale = fp32_rne(coef * inv_loss_scale)
+ * d_sq: device double, the squared norm of the unscaled gradient as zero_shard_sqnorm writes it;
+ * d_grad_scale: device float, for zero_adam_shard_step_dev_scale. One single-thread kernel on
+ * stream; nothing is read back. With the overflow flag set the norm is not finite and the scale
+ * is meaningless, but the update it feeds is then skipped.
+ * Errors: NULL or overlapping pointers; max_norm or inv_loss_scale not finite and > 0; clip_eps
+ * not finite and >= 0 -> ZERO_E_INVAL. */
+zero_status zero_clip_scale(const double* d_sq, double max_norm, double clip_eps,
+                            double inv_loss_scale, float* d_grad_scale, void* stream);
+
 /* ZeRO-3 parameter gather for one layer (P1 section 三; P2 ZeRO Stage 3; P3 core operations: with
  * parameters sharded, a layer's full parameters are rebuilt from every rank's shard before it runs
  * and the other ranks' parts are released afterwards). The gathered flat space is the nd shards of

@@ -123,8 +123,12 @@ def shard_sqnorm(acc: np.ndarray, sq_scale: float = 1.0, chunk: int = 1 << 20) -
 
 
 def clip_coefficient(total_sq: float, max_norm: float = 1.0, eps: float = 1e-6) -> float:
-    """min(1, max_norm / (||g|| + eps)), fp64. Parity unpinned (no page defines clipping)."""
-    return min(1.0, max_norm / (math.sqrt(total_sq) + eps))
+    """min(1, max_norm / (||g|| + eps)) in IEEE fp64: a zero norm with eps = 0 divides to +inf
+    (coefficient 1), an infinite norm gives 0, and a NaN quotient gives 1. Parity unpinned (no page
+    defines clipping)."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = float(np.float64(max_norm) / (np.sqrt(np.float64(total_sq)) + np.float64(eps)))
+    return min(1.0, q)
 
 
 def adam_update(p: np.ndarray, m: np.ndarray, v: np.ndarray, g: np.ndarray,

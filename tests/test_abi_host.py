@@ -175,6 +175,41 @@ def test_device_entry_points_validate_first():
     assert "overlap" in Z.zero_last_error()
 
 
+def test_device_scale_entry_points_validate_first():
+    L = Z.lib()
+    hp = Z.adam_hparams()
+    fake = 1 << 40                                   # never dereferenced: every call below is invalid
+    ok_src, k1 = _src([fake])
+    step = L.zero_adam_shard_step_dev_scale
+    # NULL grad scale (even for n = 0); grad scale inside master or the output
+    assert step(ctypes.byref(ok_src), 0, None, None, None, None, ctypes.byref(hp), None, 0, None, None) == 1
+    assert "d_grad_scale" in Z.zero_last_error()
+    assert step(ctypes.byref(ok_src), 100, fake + 4096 + 8, fake + 4096, fake + 8192, fake + 12288,
+                ctypes.byref(hp), None, 0, None, None) == 1
+    assert "grad scale" in Z.zero_last_error()
+    assert step(ctypes.byref(ok_src), 100, fake + 16384 + 4, fake + 4096, fake + 8192, fake + 12288,
+                ctypes.byref(hp), fake + 16384, Z.ZERO_BF16, None, None) == 1
+    # the rest is zero_adam_shard_step's validation
+    assert step(ctypes.byref(ok_src), 100, fake + 20000, None, fake + 8192, fake + 12288,
+                ctypes.byref(hp), None, 0, None, None) == 1
+    assert step(ctypes.byref(ok_src), 100, fake + 20000, fake + 4096, fake + 8192, fake + 12288,
+                ctypes.byref(Z.adam_hparams(step=0)), None, 0, None, None) == 1
+    assert step(ctypes.byref(ok_src), 1 << 62, fake + 20000, fake + 4096, fake + 8192, fake + 12288,
+                ctypes.byref(hp), None, 0, None, None) == 2
+    # n = 0 with a grad scale pointer: a no-op before any HIP call
+    assert step(ctypes.byref(ok_src), 0, fake, None, None, None, ctypes.byref(hp), None, 0, None, None) == 0
+    clip = L.zero_clip_scale
+    assert clip(None, 1.0, 1e-6, 1.0, fake, None) == 1
+    assert clip(fake, 1.0, 1e-6, 1.0, None, None) == 1
+    assert clip(fake, 1.0, 1e-6, 1.0, fake + 4, None) == 1          # scale inside the norm
+    assert "overlaps" in Z.zero_last_error()
+    for mn, eps, inv in ((0.0, 1e-6, 1.0), (-1.0, 1e-6, 1.0), (float("inf"), 1e-6, 1.0),
+                         (float("nan"), 1e-6, 1.0), (1.0, -1e-6, 1.0), (1.0, float("nan"), 1.0),
+                         (1.0, float("inf"), 1.0), (1.0, 1e-6, 0.0), (1.0, 1e-6, -1.0),
+                         (1.0, 1e-6, float("inf"))):
+        assert clip(fake, mn, eps, inv, fake + 8, None) == 1, (mn, eps, inv)
+
+
 def test_sq_partials_len():
     # one partial per 256-element tile, then 1024 second-level slots; no wrap-around at the top
     for n, want in ((0, 1024), (1, 1025), (256, 1025), (257, 1026), (813_491_520, 3_177_702 + 1024),

@@ -52,9 +52,12 @@ def test_fused_step_graph_replays_match_eager(n):
         assert_bits_equal(bits16(g_out), bits16(e_out), f"replay {k} params")
 
 
-def test_reduce_sqnorm_skip_graph_replays_match_eager():
+@pytest.mark.parametrize("device_clip", [False, True])
+def test_reduce_sqnorm_skip_graph_replays_match_eager(device_clip):
     """Pass 1, the squared-norm finish and pass 2 with the device skip flag, in one graph. The flag
-    is cleared by a fill kernel inside the graph (not a memset)."""
+    is cleared by a fill kernel inside the graph (not a memset). With ``device_clip`` the clip
+    scale is formed on the device between the passes (zero_clip_scale), so the graph holds the
+    whole clipped step and each replay clips by that replay's own norm."""
     n, R = 512 * 300 + 5, 16
     g = torch.Generator(device=DEV)
     g.manual_seed(2)
@@ -67,6 +70,7 @@ def test_reduce_sqnorm_skip_graph_replays_match_eager():
                     flag=torch.zeros(1, dtype=torch.int32, device=DEV),
                     parts=torch.empty(Z.zero_sq_partials_len(n), dtype=torch.float64, device=DEV),
                     sq=torch.empty(1, dtype=torch.float64, device=DEV),
+                    gs=torch.empty(1, dtype=torch.float32, device=DEV),
                     out=torch.zeros(n, dtype=torch.float16, device=DEV))
 
     h = Z.adam_hparams(step=1, lr=1e-3, weight_decay=0.01)
@@ -75,7 +79,13 @@ def test_reduce_sqnorm_skip_graph_replays_match_eager():
         b["flag"].fill_(0)
         Z.zero_reduce_shard(reps, n, b["g"], b["flag"], b["parts"], 2.0 ** -16)
         Z.zero_shard_sqnorm(None, n, 2.0 ** -16, b["parts"], b["sq"])
-        Z.zero_adam_shard_step([b["g"]], n, 2.0 ** -16, b["p"], b["m"], b["v"], h, out=b["out"], skip=b["flag"])
+        if device_clip:
+            Z.zero_clip_scale(b["sq"], 0.01, 1e-6, 2.0 ** -16, b["gs"])
+            Z.zero_adam_shard_step_dev_scale([b["g"]], n, b["gs"], b["p"], b["m"], b["v"], h,
+                                             out=b["out"], skip=b["flag"])
+        else:
+            Z.zero_adam_shard_step([b["g"]], n, 2.0 ** -16, b["p"], b["m"], b["v"], h, out=b["out"],
+                                   skip=b["flag"])
 
     gb, eb = buffers(), buffers()
     side = torch.cuda.Stream()
@@ -96,3 +106,7 @@ def test_reduce_sqnorm_skip_graph_replays_match_eager():
             assert torch.equal(a.view(torch.int16 if a.element_size() == 2 else torch.int32),
                                b.view(torch.int16 if b.element_size() == 2 else torch.int32)), (k, key)
         assert float(gb["sq"].item()) == float(eb["sq"].item()) and int(gb["flag"].item()) == 0
+        if device_clip:
+            assert gb["gs"].view(torch.int32).item() == eb["gs"].view(torch.int32).item()
+            coef = min(1.0, 0.01 / (float(gb["sq"].item()) ** 0.5 + 1e-6))
+            assert 0.0 < coef < 1.0                     # clipping is active

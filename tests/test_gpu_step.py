@@ -313,8 +313,10 @@ def test_sqnorm_from_fp32_grad():
 
 # ------------------------------------------------------------------ two-pass clip / overflow path
 
-def _two_pass(reps_np, n, master, loss_scale, max_norm, hp_kw):
-    """reduce (grad, flag, partials) -> sqnorm -> host coef -> step with skip flag."""
+def _two_pass(reps_np, n, master, loss_scale, max_norm, hp_kw, device_scale):
+    """reduce (grad, flag, partials) -> sqnorm -> clip scale -> step with skip flag. The clip scale
+    is formed on the host from the read-back norm, or on the device (zero_clip_scale feeding
+    zero_adam_shard_step_dev_scale, nothing read back before the update)."""
     d_r = [dev_rep(r, "f16") for r in reps_np]
     d_g = torch.empty(n, device=DEV)
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -322,19 +324,28 @@ def _two_pass(reps_np, n, master, loss_scale, max_norm, hp_kw):
     sq = torch.empty(1, dtype=torch.float64, device=DEV)
     Z.zero_reduce_shard(d_r, n, d_g, flag, parts, 1.0 / loss_scale)
     Z.zero_shard_sqnorm(None, n, 1.0 / loss_scale, parts, sq)
-    flag_h, sq_h = int(flag.item()), float(sq.item())
-    coef = O.clip_coefficient(sq_h, max_norm) if flag_h == 0 else 1.0
-    gs = float(np.float32(coef / loss_scale))
     d_p, d_m, d_v = dev_f32(master), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
     d_o = empty16(n, "f16", fill=0.0)
-    Z.zero_adam_shard_step([d_g], n, gs, d_p, d_m, d_v, Z.adam_hparams(**hp_kw), out=d_o, skip=flag)
-    torch.cuda.synchronize()
+    hp = Z.adam_hparams(**hp_kw)
+    if device_scale:
+        d_gs = torch.full((1,), float("nan"), device=DEV)
+        Z.zero_clip_scale(sq, max_norm, 1e-6, 1.0 / loss_scale, d_gs)
+        Z.zero_adam_shard_step_dev_scale([d_g], n, d_gs, d_p, d_m, d_v, hp, out=d_o, skip=flag)
+        torch.cuda.synchronize()
+        flag_h, sq_h, gs = int(flag.item()), float(sq.item()), float(d_gs.item())
+    else:
+        flag_h, sq_h = int(flag.item()), float(sq.item())
+        coef = O.clip_coefficient(sq_h, max_norm) if flag_h == 0 else 1.0
+        gs = float(np.float32(coef / loss_scale))
+        Z.zero_adam_shard_step([d_g], n, gs, d_p, d_m, d_v, hp, out=d_o, skip=flag)
+        torch.cuda.synchronize()
     return flag_h, sq_h, gs, bits32(d_p), bits32(d_m), bits32(d_v), bits16(d_o)
 
 
+@pytest.mark.parametrize("device_scale", [False, True])
 @pytest.mark.parametrize("inject", [False, True])
-def test_two_pass_clip_and_overflow_skip(inject):
-    """fp16 replicas holding grad * 2^16: unscale, squared norm, clip coefficient from the host,
+def test_two_pass_clip_and_overflow_skip(inject, device_scale):
+    """fp16 replicas holding grad * 2^16: unscale, squared norm, clip coefficient (host or device),
     AdamW; with an injected +inf the whole step is skipped and the state stays bit-identical."""
     n, R, ls = 6 * TILE + 321, 16, 65536.0
     rng = np.random.default_rng(31)
@@ -344,7 +355,7 @@ def test_two_pass_clip_and_overflow_skip(inject):
         reps[5, 1234] = 0x7C00
     master = (rng.standard_normal(n) * 0.02).astype(np.float32)
     hp = dict(lr=1e-3, weight_decay=0.01, step=1)
-    flag, sq, gs, p, m, v, o = _two_pass(reps, n, master, ls, 0.01, hp)
+    flag, sq, gs, p, m, v, o = _two_pass(reps, n, master, ls, 0.01, hp, device_scale)
     acc = O.replica_sum(list(reps), "f16")
     assert flag == int(O.nonfinite_flag(acc))
     if inject:
@@ -359,12 +370,63 @@ def test_two_pass_clip_and_overflow_skip(inject):
     # then checked bit for bit with that same scale
     want_gs = np.float32(coef / ls)
     assert abs(np.float32(gs) - want_gs) <= np.spacing(want_gs)
+    if device_scale:                                    # from the device's own norm, exactly
+        assert np.float32(gs) == np.float32(O.clip_coefficient(sq, 0.01) / ls)
     p2, m2, v2, o2 = O.sharded_step([acc], "f32", gs, master, np.zeros(n, np.float32),
                                     np.zeros(n, np.float32), O.AdamHParams(**hp), "f16")
     assert_bits_equal(p, f32_bits(p2), "master")
     assert_bits_equal(m, f32_bits(m2), "m")
     assert_bits_equal(v, f32_bits(v2), "v")
     assert_bits_equal(o, o2, "fp16 params")
+
+
+def test_clip_scale_matches_fp64_formula():
+    """zero_clip_scale over norms from 0 and subnormals to huge, inf and NaN, and several max_norm,
+    eps and loss scales: the device's fp32 scale equals the oracle's clip coefficient, formed in
+    correctly rounded fp64 and rounded once to fp32, bit for bit."""
+    rng = np.random.default_rng(77)
+    sqs = [0.0, 5e-324, 2.2e-308, 1e-300, 1e-12, 1e-4, 0.25, 1.0, 4.0, 1e4, 1e300, 1.7e308,
+           float("inf"), float("nan")]
+    sqs += list(10.0 ** rng.uniform(-300, 300, 60)) + list(rng.uniform(0, 4, 40))
+    cases = [(mn, eps, inv) for mn in (1.0, 0.01, 3.7) for eps in (1e-6, 0.0)
+             for inv in (2.0 ** -16, 1.0, 1.0 / 3.0)]
+    d_sq = torch.tensor(sqs, dtype=torch.float64, device=DEV)
+    for mn, eps, inv in cases:
+        out = torch.full((len(sqs),), float("nan"), device=DEV)
+        for i in range(len(sqs)):
+            Z.zero_clip_scale(d_sq[i:i + 1], mn, eps, inv, out[i:i + 1])
+        got = bits32(out)
+        want = np.array([np.float32(O.clip_coefficient(x, mn, eps) * inv) for x in sqs],
+                        dtype=np.float32).view(np.uint32)
+        assert_bits_equal(got, want, f"max_norm {mn}, eps {eps}, inv_loss_scale {inv}")
+
+
+def test_device_scale_step_equals_host_scale_step():
+    """The fused step with its grad scale read from device memory gives the bits of the same step
+    with that scale passed from the host: bf16 replicas, a ragged tail, the skip flag off and on."""
+    n, R = 9 * TILE + 77, 8
+    rng = np.random.default_rng(5)
+    reps = [dev_rep(r, "bf16") for r in _reps_np(rng, R, n, "bf16")]
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    hp = Z.adam_hparams(lr=1e-3, weight_decay=0.01, step=3)
+    for gs in (1.0, 0.37, 2.0 ** -20):
+        for skip_val in (0, 1):
+            res = []
+            for dev_scale in (False, True):
+                d_p, d_m, d_v = dev_f32(master), torch.full((n,), 1e-4, device=DEV), torch.full((n,), 1e-8, device=DEV)
+                d_o = empty16(n, "bf16", fill=0.0)
+                skip = torch.full((1,), skip_val, dtype=torch.int32, device=DEV)
+                if dev_scale:
+                    d_gs = torch.full((1,), gs, device=DEV)
+                    Z.zero_adam_shard_step_dev_scale(reps, n, d_gs, d_p, d_m, d_v, hp, out=d_o, skip=skip)
+                else:
+                    Z.zero_adam_shard_step(reps, n, gs, d_p, d_m, d_v, hp, out=d_o, skip=skip)
+                torch.cuda.synchronize()
+                res.append((bits32(d_p), bits32(d_m), bits32(d_v), bits16(d_o)))
+            for a, b, what in zip(res[0], res[1], ("master", "m", "v", "params")):
+                assert_bits_equal(b, a, f"gs {gs} skip {skip_val} {what}")
+            if skip_val:
+                assert_bits_equal(res[1][0], f32_bits(master), "skipped master")
 
 
 # --- IEEE special cases inside the update: subnormals, overflow, 0/0, inf/inf, signed zeros ----------

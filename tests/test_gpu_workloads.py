@@ -140,7 +140,9 @@ def test_llama7b_shard_full_size():
 @pytest.mark.parametrize("inject", [False, True])
 def test_llama13b_two_pass_full_size(inject):
     """Llama-13B over 16 ranks: 16 fp16 replicas holding grad * 2^16 (with 0.01% +inf injected in
-    the second case), reduce -> squared norm -> clip coefficient -> AdamW with the skip flag."""
+    the second case), reduce -> squared norm -> clip scale -> AdamW with the skip flag, enqueued
+    as the benchmark runs it: the clip scale formed on the device, nothing read back before the
+    update."""
     w = WORKLOADS["llama13b"]
     if not inject:
         w = dataclasses.replace(w, inf_rate=0.0)
@@ -159,15 +161,17 @@ def test_llama13b_two_pass_full_size(inject):
     before = {ab: tuple(bits32(inp[k][ab[0]:ab[1]]).view(np.float32) for k in ("master", "m", "v"))
               for ab in wins}
     inv_ls = 1.0 / w.loss_scale
+    d_gs = torch.full((1,), float("nan"), device=DEV)
     Z.zero_reduce_shard(inp["reps"], S, d_g, flag, parts, inv_ls)
     Z.zero_shard_sqnorm(None, S, inv_ls, parts, sq)
-    flag_h, sq_h = int(flag.item()), float(sq.item())
-    parts_h = parts.cpu().numpy()
-    coef = O.clip_coefficient(sq_h, w.max_norm) if flag_h == 0 else 1.0
-    gs = float(np.float32(coef * inv_ls))
-    Z.zero_adam_shard_step([d_g], S, gs, inp["master"], inp["m"], inp["v"],
-                           Z.adam_hparams(**_hp(w, 1)), out=d_slot, skip=flag)
+    Z.zero_clip_scale(sq, w.max_norm, 1e-6, inv_ls, d_gs)
+    Z.zero_adam_shard_step_dev_scale([d_g], S, d_gs, inp["master"], inp["m"], inp["v"],
+                                     Z.adam_hparams(**_hp(w, 1)), out=d_slot, skip=flag)
     torch.cuda.synchronize()
+    flag_h, sq_h, gs = int(flag.item()), float(sq.item()), float(d_gs.item())
+    parts_h = parts.cpu().numpy()
+    if flag_h == 0:                  # the device's scale is the oracle's formula on the device's norm
+        assert np.float32(gs) == np.float32(O.clip_coefficient(sq_h, w.max_norm) * inv_ls)
 
     # the reduced gradient and the flag, on windows
     any_bad = False

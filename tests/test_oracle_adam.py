@@ -99,6 +99,13 @@ def test_clip_coefficient_limits():
     assert O.clip_coefficient(0.0) == 1.0
     c = O.clip_coefficient(100.0, max_norm=1.0)
     assert c == pytest.approx(0.1, rel=1e-6) and c < 0.1
+    # IEEE edges: a zero norm with eps = 0 is not clipped, an infinite norm scales to 0, NaN gives 1
+    assert O.clip_coefficient(0.0, max_norm=1.0, eps=0.0) == 1.0
+    assert O.clip_coefficient(float("inf")) == 0.0
+    assert O.clip_coefficient(float("nan")) == 1.0
+    # with eps = 0 and a perfect-square norm the quotient is exact
+    assert O.clip_coefficient(16.0, max_norm=1.0, eps=0.0) == 0.25
+    assert O.clip_coefficient(2.0 ** -40, max_norm=2.0 ** -30, eps=0.0) == 2.0 ** -10
 
 
 def test_union_of_shards_equals_unsharded_tiny():

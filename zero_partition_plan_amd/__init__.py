@@ -24,6 +24,7 @@ __all__ = [
     "zero_adam_derive", "ZeroArenaArray", "zero_arena_layout", "zero_arena_alloc", "zero_arena_free",
     "arena",
     "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
+    "zero_adam_shard_step_dev_scale", "zero_clip_scale",
     "AdamStep",
     "zero_gather_params", "zero_host_adam_step", "zero_offload_step",
     "zero_status_str", "zero_last_error",
@@ -122,6 +123,9 @@ def lib() -> ctypes.CDLL:
             "zero_shard_sqnorm": [vp, u64, ctypes.c_double, vp, vp, vp],
             "zero_adam_shard_step": [P(_GradSrc), u64, ctypes.c_float, vp, vp, vp,
                                      P(ZeroAdamHParams), vp, i32, vp, vp],
+            "zero_adam_shard_step_dev_scale": [P(_GradSrc), u64, vp, vp, vp, vp,
+                                               P(ZeroAdamHParams), vp, i32, vp, vp],
+            "zero_clip_scale": [vp, ctypes.c_double, ctypes.c_double, ctypes.c_double, vp, vp],
             "zero_gather_params": [P(vp), u32, u64, u32, u64, u64, vp, vp],
             "zero_host_adam_step": [vp, u64, ctypes.c_float, vp, vp, vp, P(ZeroAdamHParams), vp, i32,
                                     u32],
@@ -315,21 +319,48 @@ def zero_shard_sqnorm(grad, n: int, sq_scale: float, partials, out, stream=None)
         _ptr(out, 1, "out", (torch.float64,)), _stream(stream)), "zero_shard_sqnorm")
 
 
+def _out_dtype(out) -> int:
+    if out is None:
+        return ZERO_F32
+    if out.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("out must be bfloat16 or float16")
+    return _TORCH_DT[out.dtype]
+
+
 def zero_adam_shard_step(reps, n: int, grad_scale: float, master, m, v, hp: ZeroAdamHParams,
                          out=None, skip=None, stream=None):
     """``out``: bf16/fp16 device tensor view starting at the rank's slot (or None)."""
     src, keep = _src(reps, n)
     f32 = (torch.float32,)
-    out_dt = ZERO_F32
-    if out is not None:
-        if out.dtype not in (torch.bfloat16, torch.float16):
-            raise TypeError("out must be bfloat16 or float16")
-        out_dt = _TORCH_DT[out.dtype]
+    out_dt = _out_dtype(out)
     _check(lib().zero_adam_shard_step(
         ctypes.byref(src), n, float(grad_scale), _ptr(master, n, "master", f32),
         _ptr(m, n, "m", f32), _ptr(v, n, "v", f32), ctypes.byref(hp),
         _ptr(out, n, "out"), out_dt, _ptr(skip, 1, "skip", (torch.int32,)), _stream(stream)),
         "zero_adam_shard_step")
+
+
+def zero_adam_shard_step_dev_scale(reps, n: int, grad_scale, master, m, v, hp: ZeroAdamHParams,
+                                   out=None, skip=None, stream=None):
+    """zero_adam_shard_step with ``grad_scale`` a float32 device tensor, read on the device (as
+    zero_clip_scale writes it)."""
+    src, keep = _src(reps, n)
+    f32 = (torch.float32,)
+    out_dt = _out_dtype(out)
+    _check(lib().zero_adam_shard_step_dev_scale(
+        ctypes.byref(src), n, _ptr(grad_scale, 1, "grad_scale", f32), _ptr(master, n, "master", f32),
+        _ptr(m, n, "m", f32), _ptr(v, n, "v", f32), ctypes.byref(hp),
+        _ptr(out, n, "out"), out_dt, _ptr(skip, 1, "skip", (torch.int32,)), _stream(stream)),
+        "zero_adam_shard_step_dev_scale")
+
+
+def zero_clip_scale(sq, max_norm: float, clip_eps: float, inv_loss_scale: float, grad_scale,
+                    stream=None):
+    """grad_scale[0] = fp32(min(1, max_norm / (sqrt(sq[0]) + clip_eps)) * inv_loss_scale), on the
+    device: ``sq`` a float64 device tensor (zero_shard_sqnorm's output), ``grad_scale`` float32."""
+    _check(lib().zero_clip_scale(
+        _ptr(sq, 1, "sq", (torch.float64,)), float(max_norm), float(clip_eps), float(inv_loss_scale),
+        _ptr(grad_scale, 1, "grad_scale", (torch.float32,)), _stream(stream)), "zero_clip_scale")
 
 
 class AdamStep:
@@ -340,11 +371,7 @@ class AdamStep:
     def __init__(self, reps, n: int, master, m, v, out=None, skip=None, stream=None):
         self._src, self._keep = _src(reps, n)
         f32 = (torch.float32,)
-        out_dt = ZERO_F32
-        if out is not None:
-            if out.dtype not in (torch.bfloat16, torch.float16):
-                raise TypeError("out must be bfloat16 or float16")
-            out_dt = _TORCH_DT[out.dtype]
+        out_dt = _out_dtype(out)
         self._tensors = (reps, master, m, v, out, skip)
         self._fn = lib().zero_adam_shard_step
         self._args = (n, _ptr(master, n, "master", f32), _ptr(m, n, "m", f32), _ptr(v, n, "v", f32))

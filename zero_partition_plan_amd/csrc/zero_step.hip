@@ -18,6 +18,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cmath>
 #include <utility>
 
 #include "zero_device.h"
@@ -198,17 +199,18 @@ __device__ __forceinline__ void adam_elem(const RepPtrs& reps, int nrep, uint64_
   if constexpr (ODT != ZERO_F32) static_cast<uint16_t*>(out)[i] = to_out1<ODT>(p);
 }
 
-template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL>
+template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL, bool DGS>
 __global__ __launch_bounds__(kAdamBlock) void k_adam_step(
     RepPtrs reps, int nrep, uint64_t first_tile, StepScalars sc, float* __restrict__ P,
     float* __restrict__ M, float* __restrict__ V, void* __restrict__ out,
-    const int32_t* __restrict__ skip, uint64_t n) {
+    const int32_t* __restrict__ skip, const float* __restrict__ dgs, uint64_t n) {
   // One tile per block and the grid is exactly the tile count (plus the remainder block with
   // TAIL): no loop bound and no per-block bound check to wait for, so a block's first loads issue
   // right after its arguments arrive.
   if constexpr (SKIP) {
     if (*skip != 0) return;
   }
+  if constexpr (DGS) sc.gs = *dgs;   // grad scale formed on the device (zero_clip_scale)
   constexpr uint64_t kTileElems = (uint64_t)kAdamBlock * 4 * ZERO_ADAM_SUB;
   if constexpr (TAIL) {
     if (blockIdx.x == gridDim.x - 1) {   // elements [tile start, n): fewer than one tile
@@ -257,8 +259,10 @@ __global__ __launch_bounds__(kBlock) void k_adam_tail(RepPtrs reps, int nrep, ui
                                                       uint64_t n, StepScalars sc,
                                                       float* __restrict__ P, float* __restrict__ M,
                                                       float* __restrict__ V, void* __restrict__ out,
-                                                      const int32_t* __restrict__ skip) {
+                                                      const int32_t* __restrict__ skip,
+                                                      const float* __restrict__ dgs) {
   if (skip != nullptr && *skip != 0) return;
+  if (dgs != nullptr) sc.gs = *dgs;
   for (uint64_t i = begin + (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
        i += (uint64_t)gridDim.x * kBlock)
     adam_elem<RDT, ODT, L2>(reps, nrep, i, sc, P, M, V, out);
@@ -394,6 +398,18 @@ __global__ __launch_bounds__(kBlock) void k_sq_finalize(const double* __restrict
   if (threadIdx.x == 0) *out = s;
 }
 
+// clip scale: q = max_norm / (sqrt(sq) + eps) in fp64, coef = min(1, q) (1 for a NaN q), and the
+// fp32 grad scale coef * inv_loss_scale rounded to nearest even. fp64 division and square root are
+// correctly rounded in this build, as on the host.
+__global__ __launch_bounds__(64) void k_clip_scale(const double* __restrict__ sq, double max_norm,
+                                                   double eps, double inv_loss_scale,
+                                                   float* __restrict__ gs) {
+  if (threadIdx.x != 0) return;
+  const double q = max_norm / (sqrt(*sq) + eps);
+  const double coef = q < 1.0 ? q : 1.0;
+  *gs = (float)(coef * inv_loss_scale);
+}
+
 // ---------------------------------------------------------------------------------------------
 // host side
 
@@ -470,6 +486,7 @@ struct AdamArgs {
   float *P, *M, *V;
   void* out;
   const int32_t* skip;
+  const float* dgs;     // device grad scale, or NULL for sc.gs
   unsigned tail_grid;
   hipStream_t stream;
   bool fused_tail;      // aligned shard with a partial last tile: k_adam_step's extra block takes it
@@ -477,9 +494,14 @@ struct AdamArgs {
 
 template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL>
 void launch_adam_grid(const AdamArgs& a, uint64_t t0, uint64_t blocks) {
-  hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, SKIP, TAIL>), dim3((unsigned)blocks),
-                     dim3(kAdamBlock), 0, a.stream, a.reps, a.nrep, t0, a.sc, a.P, a.M, a.V, a.out,
-                     a.skip, a.n);
+  if (a.dgs != nullptr)
+    hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, SKIP, TAIL, true>), dim3((unsigned)blocks),
+                       dim3(kAdamBlock), 0, a.stream, a.reps, a.nrep, t0, a.sc, a.P, a.M, a.V,
+                       a.out, a.skip, a.dgs, a.n);
+  else
+    hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, SKIP, TAIL, false>), dim3((unsigned)blocks),
+                       dim3(kAdamBlock), 0, a.stream, a.reps, a.nrep, t0, a.sc, a.P, a.M, a.V,
+                       a.out, a.skip, a.dgs, a.n);
 }
 
 template <int RDT, int ODT, bool L2, int RFIX>
@@ -516,7 +538,8 @@ void adam_kernels(const AdamArgs& a) {
   }
   if (!a.fused_tail && a.tail_begin < a.n)
     hipLaunchKernelGGL((k_adam_tail<RDT, ODT, L2>), dim3(a.tail_grid), dim3(kBlock), 0, a.stream,
-                       a.reps, a.nrep, a.tail_begin, a.n, a.sc, a.P, a.M, a.V, a.out, a.skip);
+                       a.reps, a.nrep, a.tail_begin, a.n, a.sc, a.P, a.M, a.V, a.out, a.skip,
+                       a.dgs);
 }
 
 template <int RDT, int ODT>
@@ -672,11 +695,15 @@ zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, 
   return sq_finish(n, d_partials, d_out, st, fn);
 }
 
-zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float grad_scale,
-                                 float* master, float* m, float* v, const zero_adam_hparams* hp,
-                                 void* out_param, int32_t out_dtype, const int32_t* d_skip,
-                                 void* stream) {
-  const char* fn = "zero_adam_shard_step";
+}  // extern "C"
+
+namespace {
+
+// both step entry points: grad scale from the argument (dgs == NULL) or from device memory
+zero_status adam_step_impl(const char* fn, const zero_grad_src* src, uint64_t n, float grad_scale,
+                           const float* dgs, float* master, float* m, float* v,
+                           const zero_adam_hparams* hp, void* out_param, int32_t out_dtype,
+                           const int32_t* d_skip, void* stream) {
   zero_status s = check_src(fn, src, n);
   if (s != ZERO_OK) return s;
   if (n > 0 && (!master || !m || !v))
@@ -700,6 +727,8 @@ zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float gra
     for (uint32_t r = 0; r < src->count; ++r)
       if (zero::overlaps(own[x], own_b[x], src->ptrs[r], rb))
         return zero::fail(ZERO_E_INVAL, "%s: output array %d overlaps replica %u", fn, x, r);
+    if (dgs != nullptr && zero::overlaps(own[x], own_b[x], dgs, 4))
+      return zero::fail(ZERO_E_INVAL, "%s: output array %d overlaps the grad scale", fn, x);
   }
   if (n == 0) return zero::ok();
 
@@ -714,7 +743,7 @@ zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float gra
   if (tail_grid > (uint64_t)cus * 8) tail_grid = (uint64_t)cus * 8;
   AdamArgs a{rep_ptrs(src), (int)src->count, ntiles, tail_begin, n,
              StepScalars{grad_scale, k.b1, k.b2, k.c1, k.c2, k.ss, k.bc, k.e, k.dec, k.w},
-             master, m, v, out_param, d_skip, (unsigned)tail_grid,
+             master, m, v, out_param, d_skip, dgs, (unsigned)tail_grid,
              static_cast<hipStream_t>(stream), vec && tail_n > 0};
   const int odt = out_param ? out_dtype : ZERO_F32;
   const bool l2 = hp->wd_mode == ZERO_ADAM_L2;
@@ -724,6 +753,48 @@ zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float gra
     case ZERO_F16: adam_by_out<ZERO_F16>(a, odt, l2); break;
     default: adam_by_out<ZERO_BF16>(a, odt, l2); break;
   }
+  return launched(fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float grad_scale,
+                                 float* master, float* m, float* v, const zero_adam_hparams* hp,
+                                 void* out_param, int32_t out_dtype, const int32_t* d_skip,
+                                 void* stream) {
+  return adam_step_impl("zero_adam_shard_step", src, n, grad_scale, nullptr, master, m, v, hp,
+                        out_param, out_dtype, d_skip, stream);
+}
+
+zero_status zero_adam_shard_step_dev_scale(const zero_grad_src* src, uint64_t n,
+                                           const float* d_grad_scale, float* master, float* m,
+                                           float* v, const zero_adam_hparams* hp, void* out_param,
+                                           int32_t out_dtype, const int32_t* d_skip,
+                                           void* stream) {
+  const char* fn = "zero_adam_shard_step_dev_scale";
+  if (!d_grad_scale) return zero::fail(ZERO_E_INVAL, "%s: d_grad_scale is NULL", fn);
+  return adam_step_impl(fn, src, n, 1.0f, d_grad_scale, master, m, v, hp, out_param, out_dtype,
+                        d_skip, stream);
+}
+
+zero_status zero_clip_scale(const double* d_sq, double max_norm, double clip_eps,
+                            double inv_loss_scale, float* d_grad_scale, void* stream) {
+  const char* fn = "zero_clip_scale";
+  if (!d_sq || !d_grad_scale) return zero::fail(ZERO_E_INVAL, "%s: d_sq or d_grad_scale is NULL", fn);
+  if (zero::overlaps(d_sq, 8, d_grad_scale, 4))
+    return zero::fail(ZERO_E_INVAL, "%s: d_grad_scale overlaps d_sq", fn);
+  if (!(std::isfinite(max_norm) && max_norm > 0.0))
+    return zero::fail(ZERO_E_INVAL, "%s: max_norm %g is not finite and positive", fn, max_norm);
+  if (!(std::isfinite(clip_eps) && clip_eps >= 0.0))
+    return zero::fail(ZERO_E_INVAL, "%s: clip_eps %g is not finite and non-negative", fn, clip_eps);
+  if (!(std::isfinite(inv_loss_scale) && inv_loss_scale > 0.0))
+    return zero::fail(ZERO_E_INVAL, "%s: inv_loss_scale %g is not finite and positive", fn,
+                      inv_loss_scale);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_clip_scale, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), d_sq,
+                     max_norm, clip_eps, inv_loss_scale, d_grad_scale);
   return launched(fn);
 }
 

@@ -1,6 +1,10 @@
 /* The fused step from plain C on the GPU, through the C ABI only: zero_adam_shard_step on device
  * buffers must equal zero_reduce_shard (device) followed by zero_host_adam_step (host) on the same
- * inputs, bit for bit: master, m, v and the bf16 slot. Exits 0 when they match. */
+ * inputs, bit for bit: master, m, v and the bf16 slot. Then the clipped path with nothing read
+ * back between its calls (zero_shard_sqnorm, zero_clip_scale, zero_adam_shard_step_dev_scale):
+ * the device's grad scale must equal C's own double evaluation of the clip rule on the device's
+ * norm, and the update must equal the host update with that scale. Exits 0 when all match. */
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -105,6 +109,51 @@ int main(void) {
       if (bad < 5) fprintf(stderr, "element %u differs\n", i);
       ++bad;
     }
+  }
+
+  /* the clipped path: squared norm of the reduced gradient, clip scale and update on the device */
+  {
+    const double max_norm = 1e-3, clip_eps = 1e-6, inv_scale = 0.5;
+    double *d_parts, *d_sq, sq, q, coef;
+    float *d_gs, gs_dev, gs_c;
+    HIP(hipMalloc((void**)&d_parts, zero_sq_partials_len(N) * 8));
+    HIP(hipMalloc((void**)&d_sq, 8));
+    HIP(hipMalloc((void**)&d_gs, 4));
+    HIP(hipMemcpy(d_p, p0, N * 4, hipMemcpyHostToDevice));
+    HIP(hipMemcpy(d_m, m0, N * 4, hipMemcpyHostToDevice));
+    HIP(hipMemcpy(d_v, v0, N * 4, hipMemcpyHostToDevice));
+    ZS(zero_shard_sqnorm(d_g, N, 1.0, d_parts, d_sq, NULL));
+    ZS(zero_clip_scale(d_sq, max_norm, clip_eps, inv_scale, d_gs, NULL));
+    ZS(zero_adam_shard_step_dev_scale(&src, N, d_gs, d_p, d_m, d_v, &hp, d_out, ZERO_BF16, NULL,
+                                      NULL));
+    HIP(hipDeviceSynchronize());
+    HIP(hipMemcpy(&sq, d_sq, 8, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(&gs_dev, d_gs, 4, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(p_dev, d_p, N * 4, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(m_dev, d_m, N * 4, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(v_dev, d_v, N * 4, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(out_dev, d_out, N * 2, hipMemcpyDeviceToHost));
+    q = max_norm / (sqrt(sq) + clip_eps);
+    coef = q < 1.0 ? q : 1.0;
+    gs_c = (float)(coef * inv_scale);
+    if (!(coef < 1.0) || memcmp(&gs_c, &gs_dev, 4)) {
+      fprintf(stderr, "clip scale: device %.9g, C %.9g (coef %.17g)\n", gs_dev, gs_c, coef);
+      ++bad;
+    }
+    memcpy(p_host, p0, sizeof p0);
+    memcpy(m_host, m0, sizeof m0);
+    memcpy(v_host, v0, sizeof v0);
+    ZS(zero_host_adam_step(g, N, gs_dev, p_host, m_host, v_host, &hp, out_host, ZERO_BF16, 4));
+    for (i = 0; i < N; ++i) {
+      if (memcmp(&p_dev[i], &p_host[i], 4) || memcmp(&m_dev[i], &m_host[i], 4) ||
+          memcmp(&v_dev[i], &v_host[i], 4) || out_dev[i] != out_host[i]) {
+        if (bad < 5) fprintf(stderr, "clipped step: element %u differs\n", i);
+        ++bad;
+      }
+    }
+    HIP(hipFree(d_parts));
+    HIP(hipFree(d_sq));
+    HIP(hipFree(d_gs));
   }
   for (k = 0; k < R; ++k) HIP(hipFree(d_reps[k]));
   HIP(hipFree(d_p));

@@ -1,7 +1,9 @@
 """The fused step driven from plain C through include/zero_shard.h (no Python, no torch): on device
-buffers, zero_adam_shard_step equals zero_reduce_shard followed by zero_host_adam_step, bit for bit
-(tests/capi/step_check.c). The reduce pass and the host update are each pinned to the oracle by
-the other tests."""
+buffers, zero_adam_shard_step equals zero_reduce_shard followed by zero_host_adam_step, bit for bit;
+the clipped path enqueued with nothing read back (squared norm, zero_clip_scale,
+zero_adam_shard_step_dev_scale) gives C's own double evaluation of the clip rule and the host
+update's bits (tests/capi/step_check.c). The reduce pass and the host update are each pinned to
+the oracle by the other tests."""
 
 import os
 import shutil
@@ -24,7 +26,8 @@ def test_fused_step_from_c(tmp_path):
          "-isystem", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"),
          os.path.join(ROOT, "tests", "capi", "step_check.c"), "-o", str(exe),
          "-L", LIBDIR, "-l:libzero_shard.so", f"-Wl,-rpath,{LIBDIR}",
-         "-L", os.path.join(ROCM, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"],
+         "-L", os.path.join(ROCM, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}",
+         "-lm"],
         capture_output=True, text=True)
     assert build.returncode == 0, build.stderr[-3000:]
     print("[gpu] C ABI fused step check", flush=True)

@@ -4,7 +4,8 @@ the oracle, beyond the parametrized grids.
 Step and reduce cases draw sizes up to 5000 (ragged against every tile), 1..64 replicas of any
 dtype, either output dtype or none, both decay modes, a random grad scale and step, per-array
 element offsets (so the vector path, the per-element path and the partial last tile all occur) and
-the skip flag. Gather cases draw shard counts and sizes, ranges, element sizes and source and
+the skip flag; odd seeds pass the grad scale in device memory (zero_adam_shard_step_dev_scale).
+Gather cases draw shard counts and sizes, ranges, element sizes and source and
 output offsets. Every fp32 and 16-bit result is compared bit for bit, the squared norm to 1e-10.
 """
 
@@ -76,7 +77,13 @@ def test_random_fused_step(seed):
     skip = None if c["skip"] is None else torch.full((1,), c["skip"], dtype=torch.int32, device=DEV)
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=c["wd"], wd_mode=c["mode"],
               step=c["step"])
-    Z.zero_adam_shard_step(d_reps, n, c["gs"], d_p, d_m, d_v, Z.adam_hparams(**hp), out=d_out, skip=skip)
+    if seed % 2:                       # odd seeds: the grad scale read from device memory
+        d_gs = torch.full((1,), c["gs"], dtype=torch.float32, device=DEV)
+        Z.zero_adam_shard_step_dev_scale(d_reps, n, d_gs, d_p, d_m, d_v, Z.adam_hparams(**hp),
+                                         out=d_out, skip=skip)
+    else:
+        Z.zero_adam_shard_step(d_reps, n, c["gs"], d_p, d_m, d_v, Z.adam_hparams(**hp), out=d_out,
+                               skip=skip)
     torch.cuda.synchronize()
     skipped = c["skip"] == 1
     wp, wm, wv, wo = O.sharded_step(list(reps), c["rdt"], c["gs"], p, m, v, O.AdamHParams(**hp),

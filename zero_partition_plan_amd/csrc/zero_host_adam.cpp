@@ -101,11 +101,23 @@ void run_threads(RangeFn fn, const HostStep& s, uint64_t n, uint32_t threads) {
     return;
   }
   const uint64_t per = ((n + threads - 1) / threads + 63) / 64 * 64;  // 256-byte aligned splits
+  // No exception may leave a C entry point: a range whose thread cannot be started (or whose
+  // bookkeeping cannot be allocated) runs on the calling thread instead.
   std::vector<std::thread> pool;
-  pool.reserve(threads - 1);
+  try {
+    pool.reserve(threads - 1);
+  } catch (...) {
+    fn(s, 0, n);
+    return;
+  }
   for (uint32_t t = 1; t < threads; ++t) {
     const uint64_t lo = per * t, hi = lo + per < n ? lo + per : n;
-    if (lo < hi) pool.emplace_back(fn, std::cref(s), lo, hi);
+    if (lo >= hi) continue;
+    try {
+      pool.emplace_back(fn, std::cref(s), lo, hi);
+    } catch (...) {
+      fn(s, lo, hi);
+    }
   }
   fn(s, 0, per < n ? per : n);
   for (auto& th : pool) th.join();

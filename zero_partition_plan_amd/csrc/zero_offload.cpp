@@ -8,8 +8,6 @@
 // the rank's slot on a second stream while the host works on chunk c+1.
 #include <hip/hip_runtime_api.h>
 
-#include <vector>
-
 #include "zero_host_adam.h"
 
 extern "C" {
@@ -55,7 +53,7 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
   }
   const bool l2 = hp->wd_mode == ZERO_ADAM_L2;
   const uint64_t nchunks = (n + C - 1) / C;
-  std::vector<const void*> ptrs(src->count);
+  const void* ptrs[ZERO_MAX_REPLICAS];   // one chunk's replica pointers (no allocation)
   bool sent_any[2] = {false, false};
 
   // enqueue chunk c on the GPU: replica sum into d_grad[b], copy to h_grad[b]
@@ -64,7 +62,7 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
     const int b = (int)(c & 1);
     for (uint32_t r = 0; r < src->count; ++r)
       ptrs[r] = static_cast<const char*>(src->ptrs[r]) + off * rb;
-    const zero_grad_src part{ptrs.data(), src->count, src->dtype};
+    const zero_grad_src part{ptrs, src->count, src->dtype};
     zero_status rs = zero_reduce_shard(&part, len, buf->d_grad + b * C, nullptr, nullptr, 1.0, main);
     if (rs != ZERO_OK) return rs;
     hipError_t ce = hipMemcpyAsync(buf->h_grad + b * C, buf->d_grad + b * C, len * 4,
@@ -96,6 +94,12 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
   // the call returns once every parameter copy has landed (the host buffers are then free)
   for (int b = 0; b < 2; ++b) {
     if (sent_any[b] && e == hipSuccess) e = hipEventSynchronize(sent[b]);
+  }
+  if (e != hipSuccess || s != ZERO_OK) {
+    // after a failure, still wait for whatever was enqueued (a gradient copy into h_grad, a
+    // parameter copy from h_param), so that no copy touches the caller's host buffers after return
+    (void)hipStreamSynchronize(main);
+    if (back != main) (void)hipStreamSynchronize(back);
   }
   for (int b = 0; b < 2; ++b) {
     if (got[b]) (void)hipEventDestroy(got[b]);

@@ -110,6 +110,18 @@ zero_status zero_shard_range(const zero_plan* p, uint32_t rank, uint64_t* begin,
 zero_status zero_stage_bytes(const zero_plan* p, uint32_t stage, uint32_t param_b, uint32_t grad_b,
                              uint32_t opt_b, uint64_t out[4]);
 
+/* Bytes one rank sends per training step under one stage, the communication side of the trade
+ * (P1 sections 一/二/三 and P3 stages list: ZeRO-1 and ZeRO-2 send as much as plain data
+ * parallelism, about 2N; ZeRO-3 about 1.5 times that, from all-gathering the parameters for the
+ * forward and again for the backward). Collectives are read as rings over the plan's padded
+ * buffer: one reduce-scatter or all-gather sends (nd - 1) * S elements per rank, an all-reduce
+ * twice that. DP all-reduces the gradients; ZeRO-1/2 reduce-scatter the gradients and all-gather
+ * the parameters; ZeRO-3 reduce-scatters the gradients and all-gathers the parameters twice.
+ * out[0..2] = gradient, parameter, total bytes. stage: 0 = DP, 1..3. Host only. Errors: NULL, an
+ * inconsistent plan, stage > 3 -> ZERO_E_INVAL; a byte count >= 2^64 -> ZERO_E_OVERFLOW. */
+zero_status zero_stage_comm_bytes(const zero_plan* p, uint32_t stage, uint32_t param_b,
+                                  uint32_t grad_b, uint64_t out[3]);
+
 /* The stage-choice rule of P1 section 四 (its decision tree: a card that can hold the whole model
  * takes ZeRO-1, one that can still hold parameters and gradients takes ZeRO-2, otherwise ZeRO-3 with
  * optimizer-state offload advised), read as: the smallest stage of 1..3 whose per-rank bytes

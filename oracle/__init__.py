@@ -23,8 +23,8 @@ Modules:
              Adam/AdamW update and the full per-rank step                          [P1 二; P2 Stage 1/2]
   cast       fp32 -> bf16 / fp16 round-to-nearest-even (bit patterns as uint16)  [P1 一; P3 comparisons]
   gather     ZeRO-3 gather of one layer's parameters from the rank shards         [P1 三; P3 core operations]
-  memory     per-stage model-state bytes per rank (DP, ZeRO-1/2/3) and the
-             stage-choice rule                                                  [P1 一/二/四; P3 stages]
+  memory     per-stage model-state bytes per rank (DP, ZeRO-1/2/3), the bytes a
+             rank sends per step under each stage, and the stage-choice rule  [P1 一/二/三/四; P3 stages]
 
 Parity status of each function is stated in its docstring; the clip-coefficient formula is
 "parity unpinned" (no page defines it).
@@ -45,7 +45,8 @@ from .adam import (
     unsharded_step,
 )
 from .gather import gather_range
-from .memory import MemoryEstimation, estimate_memory_per_gpu, stage_bytes_exact, STAGES, choose_stage
+from .memory import (MemoryEstimation, estimate_memory_per_gpu, stage_bytes_exact, stage_comm_bytes, STAGES,
+                     choose_stage)
 
 __all__ = [
     "Plan", "partition_plan", "shard_range",
@@ -53,5 +54,6 @@ __all__ = [
     "AdamHParams", "AdamScalars", "adam_scalars", "adam_update", "replica_sum",
     "nonfinite_flag", "shard_sqnorm", "clip_coefficient", "sharded_step", "unsharded_step",
     "gather_range",
-    "MemoryEstimation", "estimate_memory_per_gpu", "stage_bytes_exact", "STAGES", "choose_stage",
+    "MemoryEstimation", "estimate_memory_per_gpu", "stage_bytes_exact", "stage_comm_bytes", "STAGES",
+    "choose_stage",
 ]

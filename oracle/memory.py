@@ -10,6 +10,9 @@ that rule in its own form: a table of which component each stage shards.
 ``stage_bytes_exact`` is the integer variant for a concrete plan: a sharded component costs
 S (the padded shard size) elements per rank instead of N/Nd.
 
+``stage_comm_bytes`` is the other side of that trade: the bytes one rank sends per step under
+each stage, for ring collectives over the same plan.
+
 ``choose_stage`` is the stage-choice rule of [P1] section 四 (a decision tree: a card that can hold
 the whole model takes ZeRO-1; one that cannot, but can hold parameters and gradients, takes ZeRO-2;
 one that cannot even hold the parameters needs ZeRO-3, with optimizer-state offload advised). The
@@ -69,6 +72,30 @@ def stage_bytes_exact(plan: Plan, stage: int, param_b: int = 2, grad_b: int = 2,
     if total >= 1 << 64:
         raise OverflowError("byte count does not fit in 64 bits")
     return comp[0], comp[1], comp[2], total
+
+
+def stage_comm_bytes(plan: Plan, stage: int, param_b: int = 2,
+                     grad_b: int = 2) -> tuple[int, int, int]:
+    """(gradient, parameter, total) bytes one rank sends per training step; stage 0 = DP, 1..3.
+
+    [P1] section 一 and [P3] stages list: ZeRO-1 and ZeRO-2 move as much as plain data parallelism,
+    ZeRO-3 about 1.5 times as much; [P1] section 二 puts the volume of each of the first two at
+    about 2N, and section 三 traces ZeRO-3's extra to all-gathering every layer's parameters.
+    Reading: collectives run as rings over the plan's padded buffer of Nd*S elements, so one
+    reduce-scatter or one all-gather sends (Nd-1)*S elements per rank, and an all-reduce is one of
+    each. Plain DP all-reduces the gradients; ZeRO-1/2 reduce-scatter the gradients and all-gather
+    the updated parameters; ZeRO-3 all-gathers the parameters twice (forward and backward) and
+    reduce-scatters the gradients ([P1] section 三 says all-gather for the gradients in the
+    backward; the reading follows its section 二 and [P3], which say reduce-scatter).
+    """
+    if not 0 <= stage <= 3:
+        raise ValueError("stage must be 0..3")
+    one = (plan.nd - 1) * plan.shard_elems            # elements one rank sends in one ring pass
+    grad_passes, param_passes = ((2, 0), (1, 1), (1, 1), (1, 2))[stage]
+    g, w = grad_passes * one * grad_b, param_passes * one * param_b
+    if g + w >= 1 << 64:
+        raise OverflowError("byte count does not fit in 64 bits")
+    return g, w, g + w
 
 
 def choose_stage(plan: Plan, usable_bytes: int, param_b: int = 2, grad_b: int = 2,

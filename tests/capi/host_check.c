@@ -39,6 +39,10 @@ int main(void) {
         printf("stage %llu %u %u %u -> %llu %llu %llu %llu\n", (unsigned long long)ns[i], nds[i],
                aligns[i], st, (unsigned long long)by[0], (unsigned long long)by[1],
                (unsigned long long)by[2], (unsigned long long)by[3]);
+        expect(zero_stage_comm_bytes(&p, st, 2, 2, by) == ZERO_OK, "stage comm bytes");
+        printf("comm %llu %u %u %u -> %llu %llu %llu\n", (unsigned long long)ns[i], nds[i],
+               aligns[i], st, (unsigned long long)by[0], (unsigned long long)by[1],
+               (unsigned long long)by[2]);
       }
     }
   }

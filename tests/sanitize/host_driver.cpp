@@ -48,6 +48,9 @@ static void plans() {
         for (uint32_t st = 0; st <= 4; ++st) {
           const zero_status bs = zero_stage_bytes(&p, st, 2, 2, 12, by);
           EXPECT(st == 4 ? bs == ZERO_E_INVAL : (bs == ZERO_OK || bs == ZERO_E_OVERFLOW));
+          const zero_status cb = zero_stage_comm_bytes(&p, st, 2, 2, by);
+          EXPECT(st == 4 ? cb == ZERO_E_INVAL : (cb == ZERO_OK || cb == ZERO_E_OVERFLOW));
+          if (st < 4 && cb == ZERO_OK) EXPECT(by[2] == by[0] + by[1]);
         }
         zero_stage_choice c;
         const zero_status cs = zero_choose_stage(&p, 80000000000ull, 2, 2, 12, &c);

@@ -93,6 +93,24 @@ def test_stage_bytes_match_oracle():
     assert e.value.status == 2
 
 
+def test_stage_comm_bytes_match_oracle():
+    for n, nd in ((1_000_003, 4), (124_356_864, 8), (6_738_415_616, 8), (174_604_259_328, 64), (5, 1)):
+        p, op = Z.zero_partition_plan(n, nd), O.partition_plan(n, nd)
+        for stage in range(4):
+            for pb, gb in ((2, 2), (2, 4), (4, 4), (0, 2)):
+                assert Z.zero_stage_comm_bytes(p, stage, pb, gb) == O.stage_comm_bytes(op, stage, pb, gb)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_stage_comm_bytes(Z.zero_partition_plan(10, 2), 4)
+    bad = Z.zero_partition_plan(10, 2)
+    bad.pad = 3
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_stage_comm_bytes(bad, 0)
+    assert e.value.status == 1 and "inconsistent" in Z.zero_last_error()
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_stage_comm_bytes(Z.zero_partition_plan(1 << 62, 4), 3, 2, 2)
+    assert e.value.status == 2
+
+
 def test_choose_stage_matches_oracle():
     for n in (0, 1, 999, 7_000_000_000, 13_000_000_000, 70_000_000_000, 174_604_259_328):
         for nd in (1, 3, 8, 64):

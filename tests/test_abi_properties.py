@@ -41,6 +41,21 @@ def test_stage_bytes_match_oracle(n, nd, stage, pb, gb, ob):
 
 
 @SETTINGS
+@given(n=st.integers(0, 1 << 62), nd=st.integers(1, 1 << 16), stage=st.integers(0, 3),
+       pb=st.integers(0, 1 << 20), gb=st.integers(0, 1 << 20))
+def test_stage_comm_bytes_match_oracle(n, nd, stage, pb, gb):
+    plan_c, plan_o = Z.zero_partition_plan(n, nd), O.partition_plan(n, nd)
+    try:
+        want = O.stage_comm_bytes(plan_o, stage, pb, gb)
+    except OverflowError:
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_stage_comm_bytes(plan_c, stage, pb, gb)
+        assert e.value.status == 2
+        return
+    assert tuple(Z.zero_stage_comm_bytes(plan_c, stage, pb, gb)) == want
+
+
+@SETTINGS
 @given(n=st.integers(0, 1 << 40), nd=st.integers(1, 1024), usable=st.integers(0, (1 << 64) - 1))
 def test_stage_choice_matches_oracle(n, nd, usable):
     plan_c, plan_o = Z.zero_partition_plan(n, nd), O.partition_plan(n, nd)

@@ -1,6 +1,6 @@
 """The C ABI from plain C: include/zero_shard.h compiles as pedantic C99 and the host entry points,
-called from C, give the oracle's partition plan, shard ranges and per-stage bytes and the fp32 Adam
-constants the oracle derives."""
+called from C, give the oracle's partition plan, shard ranges, per-stage bytes held and sent, and
+the fp32 Adam constants the oracle derives."""
 
 import os
 import shutil
@@ -25,10 +25,10 @@ def test_host_entry_points_from_c99(tmp_path):
     assert build.returncode == 0, build.stderr[-3000:]
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, run.stderr[-3000:]
-    seen = {"plan": 0, "range": 0, "stage": 0}
+    seen = {"plan": 0, "range": 0, "stage": 0, "comm": 0}
     for line in run.stdout.splitlines():
         kind, rest = line.split(" ", 1)
-        if kind in ("plan", "range", "stage"):
+        if kind in ("plan", "range", "stage", "comm"):
             lhs, rhs = rest.split(" -> ")
             a = [int(x) for x in lhs.split()]
             got = [int(x) for x in rhs.split()]
@@ -37,6 +37,8 @@ def test_host_entry_points_from_c99(tmp_path):
                 assert got == [plan.shard_elems, plan.padded_n, plan.pad], line
             elif kind == "range":
                 assert got == list(O.shard_range(plan, a[3])), line
+            elif kind == "comm":
+                assert got == list(O.stage_comm_bytes(plan, a[3], 2, 2)), line
             else:
                 want = O.stage_bytes_exact(plan, a[3], 2, 2, 12)
                 assert got == [int(x) for x in want], line
@@ -54,4 +56,4 @@ def test_host_entry_points_from_c99(tmp_path):
             assert offs[1] >= offs[0] + 1000 and offs[2] >= offs[1] + 4000 and offs[3] == offs[2] + 4000
         elif kind == "status":
             assert rest
-    assert seen == {"plan": 4, "range": 4 + 8 + 8 + 16, "stage": 16}
+    assert seen == {"plan": 4, "range": 4 + 8 + 8 + 16, "stage": 16, "comm": 16}

@@ -3,6 +3,7 @@
 import json
 import os
 
+import numpy as np
 import pytest
 
 import oracle as O
@@ -137,3 +138,134 @@ def test_stage_choice_is_monotone():
         for u in budgets:
             st = [O.choose_stage(O.partition_plan(n, nd), u)[:2] for nd in (1, 2, 4, 8, 16, 64)]
             assert st == sorted(st, reverse=True)
+
+
+# ------------------------------------------------------------------ communication volume per step
+
+def _ring_reduce_scatter(bufs):
+    """Ring reduce-scatter, simulated: each rank's buffer is nd chunks; at step s rank r sends its
+    chunk (r - s) mod nd to rank r + 1, which adds it to its own copy. Returns each rank's chunks
+    afterwards and the elements each rank sent."""
+    nd = len(bufs)
+    chunks = [[c.copy() for c in b] for b in bufs]
+    sent = [0] * nd
+    for s in range(nd - 1):
+        msgs = [(r, (r - s) % nd, chunks[r][(r - s) % nd].copy()) for r in range(nd)]
+        for r, c, data in msgs:
+            chunks[(r + 1) % nd][c] = chunks[(r + 1) % nd][c] + data
+            sent[r] += data.size
+    return chunks, sent
+
+
+def _ring_all_gather(owned):
+    """Ring all-gather, simulated: rank r starts with chunk (r + 1) mod nd (where a ring
+    reduce-scatter leaves the reduced chunk) and at step s forwards chunk (r + 1 - s) mod nd."""
+    nd = len(owned)
+    have = [{(r + 1) % nd: owned[r].copy()} for r in range(nd)]
+    sent = [0] * nd
+    for s in range(nd - 1):
+        msgs = [(r, (r + 1 - s) % nd, have[r][(r + 1 - s) % nd]) for r in range(nd)]
+        for r, c, data in msgs:
+            have[(r + 1) % nd][c] = data.copy()
+            sent[r] += data.size
+    return have, sent
+
+
+@pytest.mark.parametrize("nd", [1, 2, 3, 4, 5, 8, 9])
+@pytest.mark.parametrize("S", [1, 3, 8])
+def test_ring_collectives_send_nd_minus_1_shards(nd, S):
+    """Brute force: a simulated ring reduce-scatter leaves every rank one distinct, fully reduced
+    chunk, a simulated all-gather then gives every rank every chunk, and each sends (nd - 1) * S
+    elements per rank: the unit the closed form counts in."""
+    rng = np.random.default_rng(nd * 100 + S)
+    bufs = [[rng.integers(-50, 50, S) for _ in range(nd)] for _ in range(nd)]
+    total = [sum(bufs[r][c] for r in range(nd)) for c in range(nd)]
+    chunks, sent = _ring_reduce_scatter(bufs)
+    owned = [chunks[r][(r + 1) % nd] for r in range(nd)]
+    for r in range(nd):
+        assert np.array_equal(owned[r], total[(r + 1) % nd])
+    assert sent == [(nd - 1) * S] * nd
+    have, sent_ag = _ring_all_gather(owned)
+    for r in range(nd):
+        assert sorted(have[r]) == list(range(nd))
+        for c in range(nd):
+            assert np.array_equal(have[r][c], total[c])
+    assert sent_ag == [(nd - 1) * S] * nd
+    # per stage, in units of one ring pass: DP all-reduce = reduce-scatter + all-gather
+    plan = O.partition_plan(nd * S, nd)
+    one = sent[0]
+    for stage, (gp, pp) in enumerate(((2, 0), (1, 1), (1, 1), (1, 2))):
+        assert O.stage_comm_bytes(plan, stage, param_b=2, grad_b=4) == (gp * one * 4, pp * one * 2,
+                                                                        gp * one * 4 + pp * one * 2)
+
+
+def check_comm_pins(comm=O.stage_comm_bytes):
+    """The pins of the per-step communication closed form, for the oracle or a planted mutant.
+
+    Unit: a simulated ring reduce-scatter (and all-gather) sends (nd - 1) * S elements per rank,
+    and an all-reduce is one of each. Pages: ZeRO-1/2 send what DP sends, ZeRO-3 1.5 times that,
+    a reduce-scatter half of an all-reduce, and ZeRO-1 all-gathers the updated parameters once
+    after the optimizer step ([P1] section 二). One rank sends nothing.
+    """
+    for nd, S in ((2, 1), (3, 4), (5, 3)):
+        rng = np.random.default_rng(nd)
+        _, sent = _ring_reduce_scatter([[rng.integers(0, 9, S) for _ in range(nd)] for _ in range(nd)])
+        plan = O.partition_plan(nd * S, nd)
+        assert comm(plan, 0, 1, 1)[0] == 2 * sent[0]            # all-reduce = reduce-scatter + all-gather
+        assert comm(plan, 1, 3, 1)[1] == 3 * sent[0]            # ZeRO-1: one all-gather of parameters
+    r12, r3 = FIG["zero12_comm_equals_dp"]["ratio"], FIG["zero3_comm_ratio"]["ratio"]
+    half = FIG["reduce_scatter_half_of_all_reduce"]["ratio"]
+    for n, nd in ((1_000_003, 4), (124_356_864, 8), (6_738_415_616, 8), (174_604_259_328, 64), (7, 16)):
+        plan = O.partition_plan(n, nd)
+        dp = comm(plan, 0, 2, 2)
+        z = [comm(plan, k, 2, 2) for k in (1, 2, 3)]
+        assert z[0][2] == r12 * dp[2] and z[1][2] == r12 * dp[2]
+        assert z[2][2] == r3 * dp[2]
+        assert z[1][0] == half * dp[0]          # the gradient reduce-scatter is half the all-reduce
+    for stage in range(4):
+        assert comm(O.partition_plan(12345, 1), stage, 2, 2) == (0, 0, 0)
+
+
+def test_comm_pins_hold_for_the_oracle():
+    check_comm_pins()
+
+
+def _comm_mutant(kind):
+    def comm(plan, stage, param_b=2, grad_b=2):
+        unit = plan.nd * plan.shard_elems if kind == "unit_nd" else (plan.nd - 1) * plan.shard_elems
+        passes = {"zero3_one_gather": ((2, 0), (1, 1), (1, 1), (1, 1)),
+                  "dp_reduce_scatter_only": ((1, 0), (1, 1), (1, 1), (1, 2)),
+                  "zero1_all_reduce": ((2, 0), (2, 0), (1, 1), (1, 2))}.get(
+            kind, ((2, 0), (1, 1), (1, 1), (1, 2)))
+        gp, pp = passes[stage]
+        g, w = gp * unit * grad_b, pp * unit * param_b
+        return g, w, g + w
+    return comm
+
+
+@pytest.mark.parametrize("kind", ["unit_nd", "zero3_one_gather", "dp_reduce_scatter_only",
+                                  "zero1_all_reduce"])
+def test_comm_mutants_are_caught(kind):
+    with pytest.raises(AssertionError):
+        check_comm_pins(_comm_mutant(kind))
+
+
+def test_comm_about_2n_per_step():
+    """ZeRO-1/2 send about 2N elements per rank per step: 2 (nd - 1) / nd of N, rising to 2."""
+    lim = FIG["zero12_comm_2n"]["elements_per_param"]
+    prev = 0.0
+    n = 2 ** 40
+    for nd in (2, 8, 64, 1024, 1 << 16):
+        plan = O.partition_plan(n, nd)
+        r = O.stage_comm_bytes(plan, 1, param_b=1, grad_b=1)[2] / n
+        assert r == 2 * (nd - 1) / nd and prev < r < lim
+        prev = r
+    assert prev == pytest.approx(lim, rel=1e-4)
+
+
+def test_comm_single_rank_sends_nothing():
+    plan = O.partition_plan(12345, 1)
+    for stage in range(4):
+        assert O.stage_comm_bytes(plan, stage) == (0, 0, 0)
+    with pytest.raises(ValueError):
+        O.stage_comm_bytes(plan, 4)

@@ -20,7 +20,8 @@ __all__ = [
     "ZeroOffloadBuffers", "lib", "lib_path", "offload_buffers",
     "ZERO_MAX_REPLICAS", "ZERO_MAX_SHARDS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
     "ZERO_ADAMW", "ZERO_ADAM_L2", "adam_hparams",
-    "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_choose_stage",
+    "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_stage_comm_bytes",
+    "zero_choose_stage",
     "zero_adam_derive", "ZeroArenaArray", "zero_arena_layout", "zero_arena_alloc", "zero_arena_free",
     "arena",
     "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
@@ -114,6 +115,7 @@ def lib() -> ctypes.CDLL:
             "zero_partition_plan": [u64, u32, u32, P(ZeroPlan)],
             "zero_shard_range": [P(ZeroPlan), u32, P(u64), P(u64)],
             "zero_stage_bytes": [P(ZeroPlan), u32, u32, u32, u32, P(u64)],
+            "zero_stage_comm_bytes": [P(ZeroPlan), u32, u32, u32, P(u64)],
             "zero_choose_stage": [P(ZeroPlan), u64, u32, u32, u32, P(ZeroStageChoice)],
             "zero_adam_derive": [P(ZeroAdamHParams), P(ZeroAdamScalars)],
             "zero_arena_layout": [P(ZeroArenaArray), u32, P(u64), P(u64)],
@@ -179,6 +181,15 @@ def zero_stage_bytes(plan: ZeroPlan, stage: int, param_b: int = 2, grad_b: int =
     out = (ctypes.c_uint64 * 4)()
     _check(lib().zero_stage_bytes(ctypes.byref(plan), stage, param_b, grad_b, opt_b, out),
            "zero_stage_bytes")
+    return tuple(int(x) for x in out)
+
+
+def zero_stage_comm_bytes(plan: ZeroPlan, stage: int, param_b: int = 2,
+                          grad_b: int = 2) -> tuple[int, int, int]:
+    """(gradient, parameter, total) bytes one rank sends per step; stage 0 = DP, 1..3."""
+    out = (ctypes.c_uint64 * 3)()
+    _check(lib().zero_stage_comm_bytes(ctypes.byref(plan), stage, param_b, grad_b, out),
+           "zero_stage_comm_bytes")
     return tuple(int(x) for x in out)
 
 

@@ -101,6 +101,30 @@ zero_status zero_stage_bytes(const zero_plan* p, uint32_t stage, uint32_t param_
   return ok();
 }
 
+// Bytes sent per rank per step: "ZeRO 优化器的三个阶段深度对比", sections 一 to 三, and "ZeRO
+// Optimization", stages list (ZeRO-1/2 send as much as data parallelism, ZeRO-3 about 1.5 times).
+// Ring collectives over the padded plan: one reduce-scatter or all-gather pass sends (nd-1)*S
+// elements per rank; each stage is a count of such passes over gradients and parameters.
+zero_status zero_stage_comm_bytes(const zero_plan* p, uint32_t stage, uint32_t param_b,
+                                  uint32_t grad_b, uint64_t out[3]) {
+  if (!p || !out) return fail(ZERO_E_INVAL, "zero_stage_comm_bytes: NULL argument");
+  if (!plan_consistent(p)) return fail(ZERO_E_INVAL, "zero_stage_comm_bytes: inconsistent plan");
+  if (stage > 3) return fail(ZERO_E_INVAL, "zero_stage_comm_bytes: stage %u > 3", stage);
+  // (gradient passes, parameter passes): DP all-reduce = reduce-scatter + all-gather of the
+  // gradients; ZeRO-1/2 reduce-scatter gradients, all-gather parameters; ZeRO-3 all-gathers the
+  // parameters for the forward and again for the backward
+  static const uint32_t kPasses[4][2] = {{2, 0}, {1, 1}, {1, 1}, {1, 2}};
+  uint64_t one, g, w, t;
+  if (!mul_u64((uint64_t)(p->nd - 1), p->shard_elems, &one) ||
+      !mul_u64(one, (uint64_t)kPasses[stage][0] * grad_b, &g) ||
+      !mul_u64(one, (uint64_t)kPasses[stage][1] * param_b, &w) || !add_u64(g, w, &t))
+    return fail(ZERO_E_OVERFLOW, "zero_stage_comm_bytes: byte count does not fit in 64 bits");
+  out[0] = g;
+  out[1] = w;
+  out[2] = t;
+  return ok();
+}
+
 // Stage choice: "ZeRO 优化器的三个阶段深度对比", section 四 (the decision tree), read as the
 // smallest stage whose per-rank bytes fit the caller's usable budget.
 zero_status zero_choose_stage(const zero_plan* p, uint64_t usable_bytes, uint32_t param_b,

@@ -191,6 +191,13 @@ zero_status zero_arena_free(void* d_ptr);
  * non-finite or negative lr/eps/wd, unknown wd_mode -> ZERO_E_INVAL. */
 zero_status zero_adam_derive(const zero_adam_hparams* hp, zero_adam_scalars* out);
 
+/* The constants of steps t = 1..count: out[t-1] is zero_adam_derive's result for hp with step = t
+ * (hp->step is ignored), bit for bit. A table for zero_adam_shard_step_dev_t, copied to the device
+ * by the caller. Host only. Errors: NULL, count == 0, or hyper-parameters zero_adam_derive rejects
+ * -> ZERO_E_INVAL. */
+zero_status zero_adam_derive_table(const zero_adam_hparams* hp, uint32_t count,
+                                   zero_adam_scalars* out);
+
 /* Length, in doubles, of the squared-norm partials buffer for a shard of n elements:
  * ceil(n / 256) per-tile partials followed by 1024 second-level slots. Host only; never fails. */
 uint64_t zero_sq_partials_len(uint64_t n);
@@ -254,6 +261,23 @@ zero_status zero_adam_shard_step_dev_scale(const zero_grad_src* src, uint64_t n,
                                            const float* d_grad_scale, float* master, float* m,
                                            float* v, const zero_adam_hparams* hp, void* out_param,
                                            int32_t out_dtype, const int32_t* d_skip, void* stream);
+
+/* The same step with its step counter also in device memory, so that a whole training step can be
+ * enqueued, or captured in a graph and replayed, without the host supplying t: each update block
+ * reads t = *d_step (device int64, t >= 1) and takes its constants from d_table[t-1] (device
+ * zero_adam_scalars[table_len], e.g. zero_adam_derive_table's; a t past the table takes its last
+ * entry, a t below 1 its first), and the grad scale from *d_grad_scale. After the update one
+ * single-thread kernel on the same stream advances *d_step by one unless d_skip is set (a skipped
+ * step does not count). With n == 0 only that advance is enqueued. wd_mode is the zero_wd_mode the
+ * table was derived for. Everything else as zero_adam_shard_step.
+ * Errors: as zero_adam_shard_step; NULL d_grad_scale, d_table or d_step, table_len == 0, an
+ * unknown wd_mode, d_step overlapping the table, the grad scale or the flag, or master, m, v or
+ * out_param overlapping any of them -> ZERO_E_INVAL. */
+zero_status zero_adam_shard_step_dev_t(const zero_grad_src* src, uint64_t n,
+                                       const float* d_grad_scale, const zero_adam_scalars* d_table,
+                                       uint32_t table_len, int64_t* d_step, int32_t wd_mode,
+                                       float* master, float* m, float* v, void* out_param,
+                                       int32_t out_dtype, const int32_t* d_skip, void* stream);
 
 /* Gradient-clipping scale for the two-pass step, formed on the device. The pages do not clip; this
  * is the usual global-norm rule, with the shard's squared norm standing for the global one:

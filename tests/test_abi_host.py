@@ -228,6 +228,57 @@ def test_device_scale_entry_points_validate_first():
         assert clip(fake, mn, eps, inv, fake + 8, None) == 1, (mn, eps, inv)
 
 
+def test_derive_table_matches_oracle_per_step():
+    for kw in (dict(lr=1e-3, weight_decay=0.01), dict(lr=3e-4, beta1=0.8, beta2=0.95, eps=1e-6,
+                                                      weight_decay=0.1, wd_mode="l2", step=77)):
+        hp = Z.adam_hparams(**kw)
+        tab = Z.zero_adam_derive_table(hp, 300)
+        for t in (1, 2, 3, 10, 11, 299, 300):
+            want = O.adam_scalars(O.AdamHParams(**{**kw, "step": t}))
+            got = tab[t - 1]
+            for f in ("b1", "b2", "c1", "c2", "ss", "bc", "e", "dec", "w"):
+                assert np.float32(getattr(got, f)).view(np.uint32) == \
+                    np.float32(getattr(want, f)).view(np.uint32), (kw, t, f)
+        dev = Z.adam_table(hp, 4, device="cpu")
+        assert dev.shape == (4, 9) and float(dev[3, 4]) == tab[3].ss and float(dev[0, 5]) == tab[0].bc
+    L = Z.lib()
+    out = (Z.ZeroAdamScalars * 2)()
+    hp = Z.adam_hparams()
+    assert L.zero_adam_derive_table(None, 2, out) == 1
+    assert L.zero_adam_derive_table(ctypes.byref(hp), 2, None) == 1
+    assert L.zero_adam_derive_table(ctypes.byref(hp), 0, out) == 1
+    assert L.zero_adam_derive_table(ctypes.byref(Z.adam_hparams(beta1=1.0)), 2, out) == 1
+
+
+def test_device_step_entry_point_validates_first():
+    L = Z.lib()
+    fake = 1 << 40                                   # never dereferenced: every call below is invalid
+    ok_src, k1 = _src([fake])
+    step = L.zero_adam_shard_step_dev_t
+    gs, tab, t = fake + 100000, fake + 200000, fake + 300000
+    P, M, V = fake + 4096, fake + 8192, fake + 12288
+    # NULL grad scale / table / step, empty table, unknown wd_mode (even for n = 0)
+    assert step(ctypes.byref(ok_src), 0, None, tab, 4, t, 0, None, None, None, None, 0, None, None) == 1
+    assert step(ctypes.byref(ok_src), 0, gs, None, 4, t, 0, None, None, None, None, 0, None, None) == 1
+    assert step(ctypes.byref(ok_src), 0, gs, tab, 4, None, 0, None, None, None, None, 0, None, None) == 1
+    assert step(ctypes.byref(ok_src), 0, gs, tab, 0, t, 0, None, None, None, None, 0, None, None) == 1
+    assert step(ctypes.byref(ok_src), 0, gs, tab, 4, t, 9, None, None, None, None, 0, None, None) == 1
+    # the step inside the table, on the grad scale or on the flag
+    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, tab + 36, 0, P, M, V, None, 0, None, None) == 1
+    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, gs, 0, P, M, V, None, 0, None, None) == 1
+    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, P, M, V, None, 0, t + 4, None) == 1
+    assert "d_step overlaps" in Z.zero_last_error()
+    # an output array over the table, the step or the grad scale
+    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, tab - 8, M, V, None, 0, None, None) == 1
+    assert "constants table" in Z.zero_last_error()
+    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, P, t - 4, V, None, 0, None, None) == 1
+    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, P, M, V, gs - 2, Z.ZERO_BF16, None, None) == 1
+    # zero_adam_shard_step's own checks still apply
+    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, None, M, V, None, 0, None, None) == 1
+    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, P, M, V, fake + 16384, Z.ZERO_F32, None, None) == 3
+    assert step(ctypes.byref(ok_src), 1 << 62, gs, tab, 4, t, 0, P, M, V, None, 0, None, None) == 2
+
+
 def test_sq_partials_len():
     # one partial per 256-element tile, then 1024 second-level slots; no wrap-around at the top
     for n, want in ((0, 1024), (1, 1025), (256, 1025), (257, 1026), (813_491_520, 3_177_702 + 1024),

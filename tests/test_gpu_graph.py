@@ -110,3 +110,71 @@ def test_reduce_sqnorm_skip_graph_replays_match_eager(device_clip):
             assert gb["gs"].view(torch.int32).item() == eb["gs"].view(torch.int32).item()
             coef = min(1.0, 0.01 / (float(gb["sq"].item()) ** 0.5 + 1e-6))
             assert 0.0 < coef < 1.0                     # clipping is active
+
+
+def test_clipped_step_with_device_counter_replays_as_successive_steps():
+    """The whole clipped two-pass step (flag fill, reduce, squared norm, clip scale, update with t
+    from a device counter, t advance) captured once: each replay is the next training step. Replays
+    match eager steps with t from the host, bit for bit; an overflow written into a replica between
+    replays makes that replay skip, with t not advancing."""
+    n, R, ls = 256 * 700 + 9, 16, 2.0 ** 16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4)
+    reps = (torch.randn(R, n, generator=g, device=DEV) * 1e-4 * ls).to(torch.float16)
+    master = torch.randn(n, generator=g, device=DEV) * 0.02
+    kw = dict(lr=1e-3, weight_decay=0.01)
+    table = Z.adam_table(Z.adam_hparams(**kw), 64, device=DEV)
+
+    def buffers():
+        return dict(p=master.clone(), m=torch.zeros(n, device=DEV), v=torch.zeros(n, device=DEV),
+                    g=torch.empty(n, device=DEV), flag=torch.zeros(1, dtype=torch.int32, device=DEV),
+                    parts=torch.empty(Z.zero_sq_partials_len(n), dtype=torch.float64, device=DEV),
+                    sq=torch.empty(1, dtype=torch.float64, device=DEV),
+                    gs=torch.empty(1, dtype=torch.float32, device=DEV),
+                    t=torch.ones(1, dtype=torch.int64, device=DEV),
+                    out=torch.zeros(n, dtype=torch.float16, device=DEV))
+
+    def front(b):
+        b["flag"].fill_(0)
+        Z.zero_reduce_shard(reps, n, b["g"], b["flag"], b["parts"], 1.0 / ls)
+        Z.zero_shard_sqnorm(None, n, 1.0 / ls, b["parts"], b["sq"])
+        Z.zero_clip_scale(b["sq"], 0.01, 1e-6, 1.0 / ls, b["gs"])
+
+    def graph_step(b):
+        front(b)
+        Z.zero_adam_shard_step_dev_t([b["g"]], n, b["gs"], table, b["t"], b["p"], b["m"], b["v"],
+                                     out=b["out"], skip=b["flag"])
+
+    gb, eb = buffers(), buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph_step(buffers())
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        graph_step(gb)
+    t_host = 1
+    saved = reps[3, 77].clone()
+    for k in range(5):
+        inject = k == 2
+        if inject:
+            reps[3, 77] = float("inf")
+        graph.replay()
+        torch.cuda.synchronize()
+        front(eb)                                      # the eager step, t from the host
+        Z.zero_adam_shard_step_dev_scale([eb["g"]], n, eb["gs"], eb["p"], eb["m"], eb["v"],
+                                         Z.adam_hparams(step=t_host, **kw), out=eb["out"], skip=eb["flag"])
+        torch.cuda.synchronize()
+        if inject:
+            reps[3, 77] = saved
+            assert int(gb["flag"].item()) == 1
+        else:
+            t_host += 1
+        assert int(gb["t"].item()) == t_host, k
+        for key in ("p", "m", "v", "g", "out"):
+            a, b = gb[key], eb[key]
+            assert torch.equal(a.view(torch.int16 if a.element_size() == 2 else torch.int32),
+                               b.view(torch.int16 if b.element_size() == 2 else torch.int32)), (k, key)
+        assert gb["gs"].view(torch.int32).item() == eb["gs"].view(torch.int32).item(), k
+    assert t_host == 5

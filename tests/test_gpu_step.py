@@ -429,6 +429,44 @@ def test_device_scale_step_equals_host_scale_step():
                 assert_bits_equal(res[1][0], f32_bits(master), "skipped master")
 
 
+def test_device_step_counter_equals_host_steps():
+    """zero_adam_shard_step_dev_t over five steps (t, constants and grad scale read on the device,
+    t advanced on the device) gives the bits of the same steps with t from the host; a skipped step
+    leaves the state and t alone; a t past the table takes its last entry; n = 0 only advances t."""
+    n, R, t0 = 7 * TILE + 45, 8, 3
+    rng = np.random.default_rng(17)
+    reps = [dev_rep(r, "bf16") for r in _reps_np(rng, R, n, "bf16")]
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    kw = dict(lr=1e-3, weight_decay=0.01, wd_mode="adamw")
+    table = Z.adam_table(Z.adam_hparams(**kw), 6, device=DEV)          # steps 1..6
+    dev = [dev_f32(master), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)]
+    host = [t.clone() for t in dev]
+    d_out, h_out = empty16(n, "bf16"), empty16(n, "bf16")
+    step = torch.full((1,), t0, dtype=torch.int64, device=DEV)
+    gs = torch.full((1,), 0.75, device=DEV)
+    skip = torch.zeros(1, dtype=torch.int32, device=DEV)
+    t_host = t0
+    for k, skipped in enumerate((False, False, True, False, False, False)):
+        skip.fill_(1 if skipped else 0)
+        Z.zero_adam_shard_step_dev_t(reps, n, gs, table, step, *dev, wd_mode="adamw", out=d_out, skip=skip)
+        # host t; past the 6-entry table the device takes entry 6, so the host passes t = 6 there
+        Z.zero_adam_shard_step(reps, n, 0.75, *host, Z.adam_hparams(step=min(t_host, 6), **kw),
+                               out=h_out, skip=skip)
+        torch.cuda.synchronize()
+        if not skipped:
+            t_host += 1
+        assert int(step.item()) == t_host, k
+        for a, b, what in zip(dev, host, ("master", "m", "v")):
+            assert_bits_equal(bits32(a), bits32(b), f"step {k} {what}")
+        assert_bits_equal(bits16(d_out), bits16(h_out), f"step {k} params")
+    assert t_host == t0 + 5 and t_host - 1 > 6                          # the last steps used the clamp
+    before = bits32(dev[0])
+    Z.zero_adam_shard_step_dev_t(reps, 0, gs, table, step, *dev)
+    torch.cuda.synchronize()
+    assert int(step.item()) == t_host + 1
+    assert_bits_equal(bits32(dev[0]), before, "n = 0")
+
+
 # --- IEEE special cases inside the update: subnormals, overflow, 0/0, inf/inf, signed zeros ----------
 
 

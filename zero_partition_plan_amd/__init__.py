@@ -25,7 +25,8 @@ __all__ = [
     "zero_adam_derive", "ZeroArenaArray", "zero_arena_layout", "zero_arena_alloc", "zero_arena_free",
     "arena",
     "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
-    "zero_adam_shard_step_dev_scale", "zero_clip_scale",
+    "zero_adam_shard_step_dev_scale", "zero_clip_scale", "zero_adam_derive_table", "adam_table",
+    "zero_adam_shard_step_dev_t",
     "AdamStep",
     "zero_gather_params", "zero_host_adam_step", "zero_offload_step",
     "zero_status_str", "zero_last_error",
@@ -128,6 +129,9 @@ def lib() -> ctypes.CDLL:
             "zero_adam_shard_step_dev_scale": [P(_GradSrc), u64, vp, vp, vp, vp,
                                                P(ZeroAdamHParams), vp, i32, vp, vp],
             "zero_clip_scale": [vp, ctypes.c_double, ctypes.c_double, ctypes.c_double, vp, vp],
+            "zero_adam_derive_table": [P(ZeroAdamHParams), u32, P(ZeroAdamScalars)],
+            "zero_adam_shard_step_dev_t": [P(_GradSrc), u64, vp, vp, u32, vp, i32, vp, vp, vp, vp,
+                                           i32, vp, vp],
             "zero_gather_params": [P(vp), u32, u64, u32, u64, u64, vp, vp],
             "zero_host_adam_step": [vp, u64, ctypes.c_float, vp, vp, vp, P(ZeroAdamHParams), vp, i32,
                                     u32],
@@ -206,6 +210,21 @@ def zero_adam_derive(hp: ZeroAdamHParams) -> ZeroAdamScalars:
     out = ZeroAdamScalars()
     _check(lib().zero_adam_derive(ctypes.byref(hp), ctypes.byref(out)), "zero_adam_derive")
     return out
+
+
+def zero_adam_derive_table(hp: ZeroAdamHParams, count: int):
+    """The constants of steps 1..count (hp.step ignored) as a ctypes array of ZeroAdamScalars."""
+    out = (ZeroAdamScalars * count)()
+    _check(lib().zero_adam_derive_table(ctypes.byref(hp), count, out), "zero_adam_derive_table")
+    return out
+
+
+def adam_table(hp: ZeroAdamHParams, count: int, device="cuda") -> torch.Tensor:
+    """zero_adam_derive_table's constants as a (count, 9) float32 tensor on ``device``, laid out
+    as the device table of zero_adam_shard_step_dev_t expects (one zero_adam_scalars per row)."""
+    tab = zero_adam_derive_table(hp, count)
+    host = torch.frombuffer(bytearray(tab), dtype=torch.float32).view(count, 9)
+    return host.to(device)
 
 
 def zero_arena_layout(arrays) -> tuple[list[int], int]:
@@ -363,6 +382,25 @@ def zero_adam_shard_step_dev_scale(reps, n: int, grad_scale, master, m, v, hp: Z
         _ptr(m, n, "m", f32), _ptr(v, n, "v", f32), ctypes.byref(hp),
         _ptr(out, n, "out"), out_dt, _ptr(skip, 1, "skip", (torch.int32,)), _stream(stream)),
         "zero_adam_shard_step_dev_scale")
+
+
+def zero_adam_shard_step_dev_t(reps, n: int, grad_scale, table, step, master, m, v,
+                               wd_mode="adamw", out=None, skip=None, stream=None):
+    """The step with its grad scale (float32 device tensor), constants table ((len, 9) float32
+    device tensor, e.g. adam_table) and step counter (int64 device tensor) all on the device; the
+    counter advances on the device unless ``skip`` is set."""
+    src, keep = _src(reps, n)
+    f32 = (torch.float32,)
+    out_dt = _out_dtype(out)
+    mode = {"adamw": ZERO_ADAMW, "l2": ZERO_ADAM_L2}.get(wd_mode, wd_mode)
+    if not isinstance(table, torch.Tensor) or table.dim() != 2 or table.shape[1] != 9:
+        raise ValueError("table must be a (len, 9) float32 device tensor")
+    _check(lib().zero_adam_shard_step_dev_t(
+        ctypes.byref(src), n, _ptr(grad_scale, 1, "grad_scale", f32),
+        _ptr(table, table.numel(), "table", f32), table.shape[0],
+        _ptr(step, 1, "step", (torch.int64,)), int(mode), _ptr(master, n, "master", f32),
+        _ptr(m, n, "m", f32), _ptr(v, n, "v", f32), _ptr(out, n, "out"), out_dt,
+        _ptr(skip, 1, "skip", (torch.int32,)), _stream(stream)), "zero_adam_shard_step_dev_t")
 
 
 def zero_clip_scale(sq, max_norm: float, clip_eps: float, inv_loss_scale: float, grad_scale,

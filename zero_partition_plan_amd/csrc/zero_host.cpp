@@ -215,6 +215,20 @@ zero_status zero_adam_derive(const zero_adam_hparams* hp, zero_adam_scalars* out
   return ok();
 }
 
+// The constants of steps 1..count, each exactly as zero_adam_derive gives it for that step.
+zero_status zero_adam_derive_table(const zero_adam_hparams* hp, uint32_t count,
+                                   zero_adam_scalars* out) {
+  if (!hp || !out) return fail(ZERO_E_INVAL, "zero_adam_derive_table: NULL argument");
+  if (count == 0) return fail(ZERO_E_INVAL, "zero_adam_derive_table: count is 0");
+  zero_adam_hparams h = *hp;
+  for (uint32_t i = 0; i < count; ++i) {
+    h.step = (int64_t)i + 1;
+    const zero_status s = zero_adam_derive(&h, &out[i]);
+    if (s != ZERO_OK) return s;
+  }
+  return ok();
+}
+
 const char* zero_status_str(zero_status s) {
   switch (s) {
     case ZERO_OK: return "ok";

@@ -67,6 +67,34 @@ struct StepScalars {
   float b1, b2, c1, c2, ss, bc, e, dec, w;
 };
 
+// Step inputs that live in device memory: the grad scale (zero_clip_scale writes it) and,
+// optionally, the step t with a table of per-step constants (entry t-1; t past the table takes
+// its last entry).
+struct DevCtl {
+  const float* gs;
+  const zero_adam_scalars* table;  // NULL: the constants passed in StepScalars
+  const int64_t* step;
+  uint32_t table_len;
+};
+
+__device__ __forceinline__ void dev_scalars(const DevCtl& dc, StepScalars& sc) {
+  sc.gs = *dc.gs;
+  if (dc.table != nullptr) {
+    const int64_t t = *dc.step;
+    const uint32_t i = t < 1 ? 0u : (t >= (int64_t)dc.table_len ? dc.table_len - 1u : (uint32_t)(t - 1));
+    const zero_adam_scalars k = dc.table[i];
+    sc.b1 = k.b1;
+    sc.b2 = k.b2;
+    sc.c1 = k.c1;
+    sc.c2 = k.c2;
+    sc.ss = k.ss;
+    sc.bc = k.bc;
+    sc.e = k.e;
+    sc.dec = k.dec;
+    sc.w = k.w;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // element conversions
 
@@ -203,14 +231,14 @@ template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL, bool DGS>
 __global__ __launch_bounds__(kAdamBlock) void k_adam_step(
     RepPtrs reps, int nrep, uint64_t first_tile, StepScalars sc, float* __restrict__ P,
     float* __restrict__ M, float* __restrict__ V, void* __restrict__ out,
-    const int32_t* __restrict__ skip, const float* __restrict__ dgs, uint64_t n) {
+    const int32_t* __restrict__ skip, DevCtl dc, uint64_t n) {
   // One tile per block and the grid is exactly the tile count (plus the remainder block with
   // TAIL): no loop bound and no per-block bound check to wait for, so a block's first loads issue
   // right after its arguments arrive.
   if constexpr (SKIP) {
     if (*skip != 0) return;
   }
-  if constexpr (DGS) sc.gs = *dgs;   // grad scale formed on the device (zero_clip_scale)
+  if constexpr (DGS) dev_scalars(dc, sc);   // grad scale (and step constants) from device memory
   constexpr uint64_t kTileElems = (uint64_t)kAdamBlock * 4 * ZERO_ADAM_SUB;
   if constexpr (TAIL) {
     if (blockIdx.x == gridDim.x - 1) {   // elements [tile start, n): fewer than one tile
@@ -260,9 +288,9 @@ __global__ __launch_bounds__(kBlock) void k_adam_tail(RepPtrs reps, int nrep, ui
                                                       float* __restrict__ P, float* __restrict__ M,
                                                       float* __restrict__ V, void* __restrict__ out,
                                                       const int32_t* __restrict__ skip,
-                                                      const float* __restrict__ dgs) {
+                                                      DevCtl dc) {
   if (skip != nullptr && *skip != 0) return;
-  if (dgs != nullptr) sc.gs = *dgs;
+  if (dc.gs != nullptr) dev_scalars(dc, sc);
   for (uint64_t i = begin + (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
        i += (uint64_t)gridDim.x * kBlock)
     adam_elem<RDT, ODT, L2>(reps, nrep, i, sc, P, M, V, out);
@@ -410,6 +438,13 @@ __global__ __launch_bounds__(64) void k_clip_scale(const double* __restrict__ sq
   *gs = (float)(coef * inv_loss_scale);
 }
 
+// the step counter after an update: t advances unless the update was skipped
+__global__ __launch_bounds__(64) void k_step_advance(int64_t* __restrict__ step,
+                                                     const int32_t* __restrict__ skip) {
+  if (threadIdx.x != 0) return;
+  if (skip == nullptr || *skip == 0) *step = *step + 1;
+}
+
 // ---------------------------------------------------------------------------------------------
 // host side
 
@@ -486,7 +521,7 @@ struct AdamArgs {
   float *P, *M, *V;
   void* out;
   const int32_t* skip;
-  const float* dgs;     // device grad scale, or NULL for sc.gs
+  DevCtl dc;            // dc.gs == NULL: everything from sc
   unsigned tail_grid;
   hipStream_t stream;
   bool fused_tail;      // aligned shard with a partial last tile: k_adam_step's extra block takes it
@@ -494,14 +529,14 @@ struct AdamArgs {
 
 template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL>
 void launch_adam_grid(const AdamArgs& a, uint64_t t0, uint64_t blocks) {
-  if (a.dgs != nullptr)
+  if (a.dc.gs != nullptr)
     hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, SKIP, TAIL, true>), dim3((unsigned)blocks),
                        dim3(kAdamBlock), 0, a.stream, a.reps, a.nrep, t0, a.sc, a.P, a.M, a.V,
-                       a.out, a.skip, a.dgs, a.n);
+                       a.out, a.skip, a.dc, a.n);
   else
     hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, SKIP, TAIL, false>), dim3((unsigned)blocks),
                        dim3(kAdamBlock), 0, a.stream, a.reps, a.nrep, t0, a.sc, a.P, a.M, a.V,
-                       a.out, a.skip, a.dgs, a.n);
+                       a.out, a.skip, a.dc, a.n);
 }
 
 template <int RDT, int ODT, bool L2, int RFIX>
@@ -539,7 +574,7 @@ void adam_kernels(const AdamArgs& a) {
   if (!a.fused_tail && a.tail_begin < a.n)
     hipLaunchKernelGGL((k_adam_tail<RDT, ODT, L2>), dim3(a.tail_grid), dim3(kBlock), 0, a.stream,
                        a.reps, a.nrep, a.tail_begin, a.n, a.sc, a.P, a.M, a.V, a.out, a.skip,
-                       a.dgs);
+                       a.dc);
 }
 
 template <int RDT, int ODT>
@@ -699,18 +734,15 @@ zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, 
 
 namespace {
 
-// both step entry points: grad scale from the argument (dgs == NULL) or from device memory
-zero_status adam_step_impl(const char* fn, const zero_grad_src* src, uint64_t n, float grad_scale,
-                           const float* dgs, float* master, float* m, float* v,
-                           const zero_adam_hparams* hp, void* out_param, int32_t out_dtype,
+// every step entry point: constants in sc0, or from device memory as dc says (dc.gs != NULL)
+zero_status adam_step_impl(const char* fn, const zero_grad_src* src, uint64_t n,
+                           const StepScalars& sc0, const DevCtl& dc, bool l2, float* master,
+                           float* m, float* v, void* out_param, int32_t out_dtype,
                            const int32_t* d_skip, void* stream) {
   zero_status s = check_src(fn, src, n);
   if (s != ZERO_OK) return s;
   if (n > 0 && (!master || !m || !v))
     return zero::fail(ZERO_E_INVAL, "%s: master, m or v is NULL", fn);
-  zero_adam_scalars k;
-  s = zero_adam_derive(hp, &k);
-  if (s != ZERO_OK) return s;
   if (out_param) {
     if (out_dtype == ZERO_F32)
       return zero::fail(ZERO_E_UNSUPPORTED, "%s: fp32 parameter output is not supported", fn);
@@ -720,6 +752,10 @@ zero_status adam_step_impl(const char* fn, const zero_grad_src* src, uint64_t n,
   const uint64_t sb = n * 4, ob = out_param ? n * 2 : 0, rb = n * zero::dtype_bytes(src->dtype);
   const void* own[4] = {master, m, v, out_param};
   const uint64_t own_b[4] = {sb, sb, sb, ob};
+  // device inputs the update reads (grad scale, constants table, step) must not be written by it
+  const void* dev_in[3] = {dc.gs, dc.table, dc.step};
+  const uint64_t dev_in_b[3] = {dc.gs ? 4u : 0u, dc.table ? (uint64_t)dc.table_len * sizeof(zero_adam_scalars) : 0u,
+                                dc.step ? 8u : 0u};
   for (int x = 0; x < 4; ++x) {
     for (int y = x + 1; y < 4; ++y)
       if (zero::overlaps(own[x], own_b[x], own[y], own_b[y]))
@@ -727,8 +763,10 @@ zero_status adam_step_impl(const char* fn, const zero_grad_src* src, uint64_t n,
     for (uint32_t r = 0; r < src->count; ++r)
       if (zero::overlaps(own[x], own_b[x], src->ptrs[r], rb))
         return zero::fail(ZERO_E_INVAL, "%s: output array %d overlaps replica %u", fn, x, r);
-    if (dgs != nullptr && zero::overlaps(own[x], own_b[x], dgs, 4))
-      return zero::fail(ZERO_E_INVAL, "%s: output array %d overlaps the grad scale", fn, x);
+    for (int d = 0; d < 3; ++d)
+      if (zero::overlaps(own[x], own_b[x], dev_in[d], dev_in_b[d]))
+        return zero::fail(ZERO_E_INVAL, "%s: output array %d overlaps the %s", fn, x,
+                          d == 0 ? "grad scale" : d == 1 ? "constants table" : "step");
   }
   if (n == 0) return zero::ok();
 
@@ -741,12 +779,10 @@ zero_status adam_step_impl(const char* fn, const zero_grad_src* src, uint64_t n,
   const uint64_t tail_begin = ntiles * kAdamTile, tail_n = n - tail_begin;
   uint64_t tail_grid = (tail_n + kBlock - 1) / kBlock;
   if (tail_grid > (uint64_t)cus * 8) tail_grid = (uint64_t)cus * 8;
-  AdamArgs a{rep_ptrs(src), (int)src->count, ntiles, tail_begin, n,
-             StepScalars{grad_scale, k.b1, k.b2, k.c1, k.c2, k.ss, k.bc, k.e, k.dec, k.w},
-             master, m, v, out_param, d_skip, dgs, (unsigned)tail_grid,
+  AdamArgs a{rep_ptrs(src), (int)src->count, ntiles, tail_begin, n, sc0,
+             master, m, v, out_param, d_skip, dc, (unsigned)tail_grid,
              static_cast<hipStream_t>(stream), vec && tail_n > 0};
   const int odt = out_param ? out_dtype : ZERO_F32;
-  const bool l2 = hp->wd_mode == ZERO_ADAM_L2;
   (void)hipGetLastError();
   switch (src->dtype) {
     case ZERO_F32: adam_by_out<ZERO_F32>(a, odt, l2); break;
@@ -754,6 +790,20 @@ zero_status adam_step_impl(const char* fn, const zero_grad_src* src, uint64_t n,
     default: adam_by_out<ZERO_BF16>(a, odt, l2); break;
   }
   return launched(fn);
+}
+
+// the host-step entry points: constants derived from hp on the host
+zero_status adam_step_host_t(const char* fn, const zero_grad_src* src, uint64_t n,
+                             float grad_scale, const float* d_grad_scale, float* master, float* m,
+                             float* v, const zero_adam_hparams* hp, void* out_param,
+                             int32_t out_dtype, const int32_t* d_skip, void* stream) {
+  zero_adam_scalars k;
+  const zero_status s = zero_adam_derive(hp, &k);
+  if (s != ZERO_OK) return s;
+  const StepScalars sc{grad_scale, k.b1, k.b2, k.c1, k.c2, k.ss, k.bc, k.e, k.dec, k.w};
+  const DevCtl dc{d_grad_scale, nullptr, nullptr, 0};
+  return adam_step_impl(fn, src, n, sc, dc, hp->wd_mode == ZERO_ADAM_L2, master, m, v, out_param,
+                        out_dtype, d_skip, stream);
 }
 
 }  // namespace
@@ -764,8 +814,8 @@ zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float gra
                                  float* master, float* m, float* v, const zero_adam_hparams* hp,
                                  void* out_param, int32_t out_dtype, const int32_t* d_skip,
                                  void* stream) {
-  return adam_step_impl("zero_adam_shard_step", src, n, grad_scale, nullptr, master, m, v, hp,
-                        out_param, out_dtype, d_skip, stream);
+  return adam_step_host_t("zero_adam_shard_step", src, n, grad_scale, nullptr, master, m, v, hp,
+                          out_param, out_dtype, d_skip, stream);
 }
 
 zero_status zero_adam_shard_step_dev_scale(const zero_grad_src* src, uint64_t n,
@@ -775,8 +825,34 @@ zero_status zero_adam_shard_step_dev_scale(const zero_grad_src* src, uint64_t n,
                                            void* stream) {
   const char* fn = "zero_adam_shard_step_dev_scale";
   if (!d_grad_scale) return zero::fail(ZERO_E_INVAL, "%s: d_grad_scale is NULL", fn);
-  return adam_step_impl(fn, src, n, 1.0f, d_grad_scale, master, m, v, hp, out_param, out_dtype,
-                        d_skip, stream);
+  return adam_step_host_t(fn, src, n, 1.0f, d_grad_scale, master, m, v, hp, out_param, out_dtype,
+                          d_skip, stream);
+}
+
+zero_status zero_adam_shard_step_dev_t(const zero_grad_src* src, uint64_t n,
+                                       const float* d_grad_scale, const zero_adam_scalars* d_table,
+                                       uint32_t table_len, int64_t* d_step, int32_t wd_mode,
+                                       float* master, float* m, float* v, void* out_param,
+                                       int32_t out_dtype, const int32_t* d_skip, void* stream) {
+  const char* fn = "zero_adam_shard_step_dev_t";
+  if (!d_grad_scale || !d_table || !d_step)
+    return zero::fail(ZERO_E_INVAL, "%s: d_grad_scale, d_table or d_step is NULL", fn);
+  if (table_len == 0) return zero::fail(ZERO_E_INVAL, "%s: empty constants table", fn);
+  if (wd_mode != ZERO_ADAMW && wd_mode != ZERO_ADAM_L2)
+    return zero::fail(ZERO_E_INVAL, "%s: unknown wd_mode %d", fn, wd_mode);
+  const uint64_t tb = (uint64_t)table_len * sizeof(zero_adam_scalars);
+  if (zero::overlaps(d_step, 8, d_table, tb) || zero::overlaps(d_step, 8, d_grad_scale, 4) ||
+      (d_skip && zero::overlaps(d_step, 8, d_skip, 4)))
+    return zero::fail(ZERO_E_INVAL, "%s: d_step overlaps the table, the grad scale or the flag", fn);
+  const StepScalars sc{1.0f, 0, 0, 0, 0, 0, 0, 0, 0, 0};   // all read from the table
+  const DevCtl dc{d_grad_scale, d_table, d_step, table_len};
+  zero_status s = adam_step_impl(fn, src, n, sc, dc, wd_mode == ZERO_ADAM_L2, master, m, v,
+                                 out_param, out_dtype, d_skip, stream);
+  if (s != ZERO_OK) return s;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_step_advance, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), d_step,
+                     d_skip);
+  return launched(fn);
 }
 
 zero_status zero_clip_scale(const double* d_sq, double max_norm, double clip_eps,

@@ -4,7 +4,9 @@ the oracle, beyond the parametrized grids.
 Step and reduce cases draw sizes up to 5000 (ragged against every tile), 1..64 replicas of any
 dtype, either output dtype or none, both decay modes, a random grad scale and step, per-array
 element offsets (so the vector path, the per-element path and the partial last tile all occur) and
-the skip flag; odd seeds pass the grad scale in device memory (zero_adam_shard_step_dev_scale).
+the skip flag; odd seeds pass the grad scale in device memory (zero_adam_shard_step_dev_scale),
+and every fourth seed also the step, with constants tables of 1, 7 or 2500 entries
+(zero_adam_shard_step_dev_t).
 Gather cases draw shard counts and sizes, ranges, element sizes and source and
 output offsets. Every fp32 and 16-bit result is compared bit for bit, the squared norm to 1e-10.
 """
@@ -77,7 +79,16 @@ def test_random_fused_step(seed):
     skip = None if c["skip"] is None else torch.full((1,), c["skip"], dtype=torch.int32, device=DEV)
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=c["wd"], wd_mode=c["mode"],
               step=c["step"])
-    if seed % 2:                       # odd seeds: the grad scale read from device memory
+    d_t = None
+    if seed % 4 == 3:                  # the grad scale and the step from device memory
+        d_gs = torch.full((1,), c["gs"], dtype=torch.float32, device=DEV)
+        table_len = [1, 7, 2500][seed // 4 % 3]      # shorter tables clamp t to their last entry
+        table = Z.adam_table(Z.adam_hparams(**hp), table_len, device=DEV)
+        d_t = torch.full((1,), c["step"], dtype=torch.int64, device=DEV)
+        Z.zero_adam_shard_step_dev_t(d_reps, n, d_gs, table, d_t, d_p, d_m, d_v, wd_mode=c["mode"],
+                                     out=d_out, skip=skip)
+        hp["step"] = min(c["step"], table_len)
+    elif seed % 2:                     # the grad scale read from device memory
         d_gs = torch.full((1,), c["gs"], dtype=torch.float32, device=DEV)
         Z.zero_adam_shard_step_dev_scale(d_reps, n, d_gs, d_p, d_m, d_v, Z.adam_hparams(**hp),
                                          out=d_out, skip=skip)
@@ -85,6 +96,8 @@ def test_random_fused_step(seed):
         Z.zero_adam_shard_step(d_reps, n, c["gs"], d_p, d_m, d_v, Z.adam_hparams(**hp), out=d_out,
                                skip=skip)
     torch.cuda.synchronize()
+    if d_t is not None:
+        assert int(d_t.item()) == c["step"] + (0 if c["skip"] == 1 else 1)
     skipped = c["skip"] == 1
     wp, wm, wv, wo = O.sharded_step(list(reps), c["rdt"], c["gs"], p, m, v, O.AdamHParams(**hp),
                                     c["odt"], skip=skipped)

@@ -3,7 +3,9 @@
  * inputs, bit for bit: master, m, v and the bf16 slot. Then the clipped path with nothing read
  * back between its calls (zero_shard_sqnorm, zero_clip_scale, zero_adam_shard_step_dev_scale):
  * the device's grad scale must equal C's own double evaluation of the clip rule on the device's
- * norm, and the update must equal the host update with that scale. Exits 0 when all match. */
+ * norm, and the update must equal the host update with that scale; so must the same update with
+ * t on the device (zero_adam_shard_step_dev_t), which also advances the counter. Exits 0 when all
+ * match. */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -150,6 +152,44 @@ int main(void) {
         if (bad < 5) fprintf(stderr, "clipped step: element %u differs\n", i);
         ++bad;
       }
+    }
+
+    /* the same clipped update with t on the device: a table of the constants of steps 1..8 built
+     * by zero_adam_derive_table, the counter at hp.step, advanced by the call */
+    {
+      zero_adam_scalars table[8];
+      zero_adam_scalars* d_table;
+      int64_t t = hp.step, *d_t;
+      ZS(zero_adam_derive_table(&hp, 8, table));
+      HIP(hipMalloc((void**)&d_table, sizeof table));
+      HIP(hipMalloc((void**)&d_t, 8));
+      HIP(hipMemcpy(d_table, table, sizeof table, hipMemcpyHostToDevice));
+      HIP(hipMemcpy(d_t, &t, 8, hipMemcpyHostToDevice));
+      HIP(hipMemcpy(d_p, p0, N * 4, hipMemcpyHostToDevice));
+      HIP(hipMemcpy(d_m, m0, N * 4, hipMemcpyHostToDevice));
+      HIP(hipMemcpy(d_v, v0, N * 4, hipMemcpyHostToDevice));
+      ZS(zero_adam_shard_step_dev_t(&src, N, d_gs, d_table, 8, d_t, ZERO_ADAMW, d_p, d_m, d_v,
+                                    d_out, ZERO_BF16, NULL, NULL));
+      HIP(hipDeviceSynchronize());
+      HIP(hipMemcpy(&t, d_t, 8, hipMemcpyDeviceToHost));
+      HIP(hipMemcpy(p_dev, d_p, N * 4, hipMemcpyDeviceToHost));
+      HIP(hipMemcpy(m_dev, d_m, N * 4, hipMemcpyDeviceToHost));
+      HIP(hipMemcpy(v_dev, d_v, N * 4, hipMemcpyDeviceToHost));
+      HIP(hipMemcpy(out_dev, d_out, N * 2, hipMemcpyDeviceToHost));
+      if (t != hp.step + 1) {
+        fprintf(stderr, "step counter: %lld after the call, %lld expected\n", (long long)t,
+                (long long)(hp.step + 1));
+        ++bad;
+      }
+      for (i = 0; i < N; ++i) {
+        if (memcmp(&p_dev[i], &p_host[i], 4) || memcmp(&m_dev[i], &m_host[i], 4) ||
+            memcmp(&v_dev[i], &v_host[i], 4) || out_dev[i] != out_host[i]) {
+          if (bad < 5) fprintf(stderr, "device-step update: element %u differs\n", i);
+          ++bad;
+        }
+      }
+      HIP(hipFree(d_table));
+      HIP(hipFree(d_t));
     }
     HIP(hipFree(d_parts));
     HIP(hipFree(d_sq));

@@ -13,12 +13,14 @@ import oracle as O
 import zero_partition_plan_amd as Z
 from gpu_util import (DEV, assert_bits_equal, assert_bits_equal_nan, banner, bits16, bits32, dev_f32,
                       dev_rep, empty16, f32_bits)
+from cast_check import check_cast_slice
 from workloads import WORKLOADS
 from workloads import host as H
 from workloads.extremes import EXTREME_CASES, f16_all_patterns, f32_patterns, mixed_state
 
 pytestmark = pytest.mark.gpu
 
+_T16 = {"bf16": torch.bfloat16, "f16": torch.float16}
 TILE = 256  # elements per tile of both the reduce and the Adam kernel (64 threads x 4)
 
 
@@ -170,6 +172,35 @@ def test_cast_edges_through_the_kernel():
                         dict(lr=1e-3, weight_decay=0.0, step=1), out_dtype)
         assert_bits_equal(got[0], f32_bits(x), "master unchanged")
         assert_bits_equal(got[3], cast(x), f"cast {out_dtype}")
+
+
+def test_cast_of_every_fp32_pattern_through_the_kernel():
+    """All 2^32 fp32 patterns as the master copy, in chunks of 2^28, through the fused update with
+    zero gradient, zero state and wd = 0 (so p is unchanged up to quieting a NaN) into both 16-bit
+    outputs: every non-NaN pattern's cast equals the oracle's bit for bit, and every NaN stays a
+    NaN (its payload bits are not the oracle's to fix). The host comparison runs on 16 threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    chunk, sub = 1 << 28, 1 << 24
+    zeros = torch.zeros(chunk, device=DEV)
+    m, v = torch.zeros(chunk, device=DEV), torch.zeros(chunk, device=DEV)
+    outs = {dt: torch.empty(chunk, dtype=_T16[dt], device=DEV) for dt in ("bf16", "f16")}
+    hp = Z.adam_hparams(lr=1e-3, weight_decay=0.0, step=1)
+    with ThreadPoolExecutor(16) as pool:
+        for c in range(1 << 4):
+            banner(f"cast of every fp32 pattern: chunk {c} of 16")
+            lo = c * chunk
+            signed_lo = lo - (1 << 32) if lo >= 1 << 31 else lo   # each chunk lies in one half
+            d_p = torch.arange(signed_lo, signed_lo + chunk, dtype=torch.int64, device=DEV)
+            d_p = d_p.to(torch.int32).view(torch.float32)
+            for out in outs.values():
+                Z.zero_adam_shard_step([zeros], chunk, 1.0, d_p, m, v, hp, out=out)
+            got = {dt: bits16(out) for dt, out in outs.items()}
+            got_p = bits32(d_p)
+            jobs = [pool.submit(check_cast_slice, lo + a, {dt: g[a:a + sub] for dt, g in got.items()},
+                                got_p[a:a + sub]) for a in range(0, chunk, sub)]
+            errors = [e for e in (j.result() for j in jobs) if e]
+            assert not errors, errors[0]
+            del d_p
 
 
 def test_skip_flag():

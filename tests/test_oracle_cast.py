@@ -113,3 +113,30 @@ def test_widen_round_trips_exactly():
     wh = O.widen_fp16(b)
     ok = ~np.isnan(wh)
     assert np.array_equal(wh[ok].astype(np.float64), _decode(b, 5, 10)[ok])
+
+
+def test_cast_slice_checker_catches_planted_mistakes():
+    """The checker behind the exhaustive GPU cast test: silent on the oracle's own casts (any NaN
+    payload allowed), loud on a wrong bit, a NaN turned into infinity, or a changed master."""
+    from cast_check import check_cast_slice
+    lo = 0x7F7FFF00                         # the top of the finite range, infinity and NaNs
+    pats = np.arange(lo, lo + 4096, dtype=np.uint64).astype(np.uint32)
+    x = pats.view(np.float32)
+    good = {"bf16": O.cast_bf16_rne(x), "f16": O.cast_fp16_rne(x)}
+    assert check_cast_slice(lo, good, pats.copy()) is None
+    nan = (pats & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    quiet = {"bf16": np.uint16(0x0040), "f16": np.uint16(0x0200)}       # another NaN payload
+    payload = {k: np.where(nan, v | quiet[k], v) for k, v in good.items()}
+    assert any((payload[k] != good[k]).any() for k in good)
+    assert check_cast_slice(lo, payload, pats.copy()) is None        # NaN payloads are free
+    for dt in ("bf16", "f16"):
+        bad = dict(good)
+        bad[dt] = good[dt].copy()
+        bad[dt][10] ^= 1                                              # a finite pattern's cast
+        assert "casts to" in check_cast_slice(lo, bad, pats.copy())
+        bad[dt] = good[dt].copy()
+        bad[dt][np.argmax(nan)] = 0x7F80 if dt == "bf16" else 0x7C00   # NaN -> infinity
+        assert "NaN" in check_cast_slice(lo, bad, pats.copy())
+    p2 = pats.copy()
+    p2[3] ^= 1
+    assert check_cast_slice(lo, good, p2) == "non-NaN master changed"

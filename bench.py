@@ -17,7 +17,7 @@ Prints one JSON line (see the fields below). Flags:
                    gather7b (ZeRO-3: every Llama-7B layer gathered from its 8 rank shards),
                    offload7b (ZeRO-Offload: the 7B shard's Adam state in host memory)
   --placement P    arena (default) or separate: every array of the step in its own allocation
-  --no-context     skip the context legs (copy ceiling, separate-placement step, cold launches)
+  --no-context     skip the context legs (copy ceiling, separate-placement step, cold launches, graph replay)
   --cpu-seconds S  budget of the oracle's CPU baseline (default 12; 0 skips it)
   --copy-calib MB  also run a plain device copy of MB MiB 5 times (for counter calibration)
   --summarize      (no GPU) turn the rocprofv3 CSVs of the profile commands into the summaries
@@ -553,6 +553,57 @@ def cold_launches(st, reps=10):
     return ms
 
 
+def graph_steps(st, steps=50):
+    """The fused step captured once in a graph with its grad scale, step counter and constants table
+    on the device (zero_adam_shard_step_dev_t), replayed as successive steps, against the same
+    number of eager steps through AdamStep: ms per step of each, for shards small enough that
+    launch overhead shows."""
+    import torch
+
+    import zero_partition_plan_amd as Z
+    w, inp, S = st["w"], st["inp"], st["S"]
+    hp = Z.adam_hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                        weight_decay=w.weight_decay, wd_mode=w.wd_mode)
+    table = Z.adam_table(hp, st["t"] + 2 * steps + 8)
+    gs = torch.ones(1, device="cuda")
+    t_dev = torch.full((1,), st["t"], dtype=torch.int64, device="cuda")
+
+    def one():
+        Z.zero_adam_shard_step_dev_t(inp["reps"], S, gs, table, t_dev, inp["master"], inp["m"],
+                                     inp["v"], wd_mode=w.wd_mode, out=st["slot"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one()                              # warm the library off the capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = new_event(True), new_event()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / steps
+    st["t"] = int(t_dev.item())
+    eager = Spans(False)
+    step_fused(st, eager)
+    torch.cuda.synchronize()
+    e0, e1 = new_event(True), new_event()
+    for _ in range(steps):
+        step_fused(st, eager)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / steps
+    del graph
+    return {"graph_ms_per_step": graph_ms, "eager_ms_per_step": eager_ms, "steps": steps,
+            "note": "one captured step (the update and the on-device step advance) replayed as "
+                    "successive steps, against as many eager calls through the Python binding"}
+
+
 def copy_ceiling(gib: int = 4):
     """A plain device copy of `gib` GiB by the library's own copy kernel (one shard, gathered whole)."""
     import torch
@@ -788,7 +839,8 @@ def main(argv=None):
                     help="arrays of the step in one arena laid out by zero_arena_layout, or each in "
                          "its own allocation")
     ap.add_argument("--no-context", action="store_true",
-                    help="skip the context legs (copy ceiling, separate-placement step, cold launches), "
+                    help="skip the context legs (copy ceiling, separate-placement step, cold launches, graph "
+                         "replay), "
                          "so that a profiler sees only the timed step's launches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle's CPU baseline (0 skips it)")
@@ -913,6 +965,11 @@ def main(argv=None):
                         "roofline figures above are warm (back-to-back launches)"}
         log(f"cold launches: median {cold['median_ms']:.4f} ms -> {cold['gbs_at_median']:.0f} GB/s")
     context = None
+    if args.workload == "gpt2" and not args.no_context:
+        context = {"graph": graph_steps(st)}
+        gr = context["graph"]
+        log(f"graph replay: {gr['graph_ms_per_step']:.4f} ms per step, eager "
+            f"{gr['eager_ms_per_step']:.4f} ms per step")
     if args.workload == "gather7b" and not args.no_context:
         nvtx.range_push("context legs")
         context = {"prefetch": gather_prefetch_context(st)}

@@ -75,6 +75,23 @@ def test_adam_constants_match_oracle(lr, b1, b2, eps, wd, step, mode):
         assert g.view(np.uint32) == w.view(np.uint32) or (np.isnan(g) and np.isnan(w)), (f, g, w)
 
 
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(lr=st.floats(0, 10), b1=st.floats(0, 0.9999), b2=st.floats(0, 0.99999),
+       eps=st.floats(0, 1), wd=st.floats(0, 1), count=st.integers(1, 3000),
+       mode=st.sampled_from(["adamw", "l2"]))
+def test_adam_constants_table_matches_oracle(lr, b1, b2, eps, wd, count, mode):
+    """Every entry t of zero_adam_derive_table is the oracle's constants for step t, bit for bit."""
+    hp = dict(lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd, wd_mode=mode)
+    tab = Z.zero_adam_derive_table(Z.adam_hparams(**hp), count)
+    got = np.frombuffer(bytes(tab), dtype=np.float32).reshape(count, 9)
+    ts = sorted(t for t in {1, 2, count, (count + 1) // 2, 17} if t <= count)
+    for t in ts:
+        k = O.adam_scalars(O.AdamHParams(**hp, step=t))
+        want = np.float32([k.b1, k.b2, k.c1, k.c2, k.ss, k.bc, k.e, k.dec, k.w])
+        same = (got[t - 1].view(np.uint32) == want.view(np.uint32)) | (np.isnan(got[t - 1]) & np.isnan(want))
+        assert same.all(), (t, got[t - 1], want)
+
+
 arrays = st.lists(st.tuples(st.integers(0, 1 << 34), st.floats(0, 1), st.integers(0, 5),
                             st.sampled_from([2, 4])), min_size=1, max_size=64)
 

@@ -184,14 +184,17 @@ zero_status zero_arena_alloc(uint64_t bytes, void** d_ptr, int32_t* contiguous);
  * with it (synchronise first). Errors: a HIP failure -> ZERO_E_HIP. */
 zero_status zero_arena_free(void* d_ptr);
 
-/* The fp32 constants of step hp->step, each formed in fp64 and rounded once:
+/* The fp32 constants of step hp->step of Adam with bias correction (Kingma and Ba's algorithm,
+ * with AdamW's decoupled decay: the pages name Adam and its fp32 state, P1 sections 一/二 and P2
+ * ZeRO Stage 1, but print no equations), each formed in fp64 and rounded once:
  * b1 = f32(beta1), b2 = f32(beta2), c1 = f32(1-beta1), c2 = f32(1-beta2),
  * ss = f32(lr / (1 - pow(beta1, t))), bc = f32(sqrt(1 - pow(beta2, t))), e = f32(eps),
  * dec = f32(1 - lr*wd), w = f32(wd). Host only. Errors: NULL, step < 1, beta outside [0, 1),
  * non-finite or negative lr/eps/wd, unknown wd_mode -> ZERO_E_INVAL. */
 zero_status zero_adam_derive(const zero_adam_hparams* hp, zero_adam_scalars* out);
 
-/* The constants of steps t = 1..count: out[t-1] is zero_adam_derive's result for hp with step = t
+/* The constants of steps t = 1..count (the same algorithm as zero_adam_derive, whose passages it
+ * follows): out[t-1] is zero_adam_derive's result for hp with step = t
  * (hp->step is ignored), bit for bit. A table for zero_adam_shard_step_dev_t, copied to the device
  * by the caller. Host only. Errors: NULL, count == 0, or hyper-parameters zero_adam_derive rejects
  * -> ZERO_E_INVAL. */
@@ -251,10 +254,11 @@ zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float gra
                                  void* out_param, int32_t out_dtype, const int32_t* d_skip,
                                  void* stream);
 
-/* The same step with its grad scale read from device memory: *d_grad_scale (device float) is read
- * once per launch in place of a host grad_scale, as zero_clip_scale writes it. With it the
- * two-pass step (zero_reduce_shard, zero_shard_sqnorm, zero_clip_scale, this call) is enqueued
- * with nothing read back to the host between its passes, and can be captured in a graph.
+/* The step of zero_adam_shard_step (P1 section 二; P2 ZeRO Stage 1/2) with its grad scale read from
+ * device memory: *d_grad_scale (device float) is read once per launch in place of a host
+ * grad_scale, as zero_clip_scale writes it. With it the two-pass step (zero_reduce_shard,
+ * zero_shard_sqnorm, zero_clip_scale, this call) is enqueued with nothing read back to the host
+ * between its passes, and can be captured in a graph.
  * Everything else is as zero_adam_shard_step. Errors: as zero_adam_shard_step, plus d_grad_scale
  * NULL or overlapping master, m, v or out_param -> ZERO_E_INVAL. */
 zero_status zero_adam_shard_step_dev_scale(const zero_grad_src* src, uint64_t n,
@@ -262,11 +266,12 @@ zero_status zero_adam_shard_step_dev_scale(const zero_grad_src* src, uint64_t n,
                                            float* v, const zero_adam_hparams* hp, void* out_param,
                                            int32_t out_dtype, const int32_t* d_skip, void* stream);
 
-/* The same step with its step counter also in device memory, so that a whole training step can be
- * enqueued, or captured in a graph and replayed, without the host supplying t: each update block
- * reads t = *d_step (device int64, t >= 1) and takes its constants from d_table[t-1] (device
- * zero_adam_scalars[table_len], e.g. zero_adam_derive_table's; a t past the table takes its last
- * entry, a t below 1 its first), and the grad scale from *d_grad_scale. After the update one
+/* The step of zero_adam_shard_step (P1 section 二; P2 ZeRO Stage 1/2) with its step counter also in
+ * device memory, so that a whole training step can be enqueued, or captured in a graph and
+ * replayed, without the host supplying t: each update block reads t = *d_step (device int64,
+ * t >= 1) and takes its constants from d_table[t-1] (device zero_adam_scalars[table_len], e.g.
+ * zero_adam_derive_table's; a t past the table takes its last entry, a t below 1 its first), and
+ * the grad scale from *d_grad_scale. After the update one
  * single-thread kernel on the same stream advances *d_step by one unless d_skip is set (a skipped
  * step does not count). With n == 0 only that advance is enqueued. wd_mode is the zero_wd_mode the
  * table was derived for. Everything else as zero_adam_shard_step.

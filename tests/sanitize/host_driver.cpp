@@ -87,6 +87,22 @@ static void derive() {
   hp.wd_mode = 7;
   EXPECT(zero_adam_derive(&hp, &k) == ZERO_E_INVAL);
   EXPECT(zero_adam_derive(NULL, &k) == ZERO_E_INVAL);
+  // the per-step table: every entry equals the single-step call, on a heap array sized exactly
+  hp.wd_mode = ZERO_ADAMW;
+  const uint32_t count = 3000;
+  zero_adam_scalars* tab = new zero_adam_scalars[count];
+  EXPECT(zero_adam_derive_table(&hp, count, tab) == ZERO_OK);
+  for (uint32_t t = 1; t <= count; t += 37) {
+    hp.step = t;
+    EXPECT(zero_adam_derive(&hp, &k) == ZERO_OK);
+    EXPECT(memcmp(&k, &tab[t - 1], sizeof k) == 0);
+  }
+  EXPECT(zero_adam_derive_table(&hp, 0, tab) == ZERO_E_INVAL);
+  EXPECT(zero_adam_derive_table(NULL, 1, tab) == ZERO_E_INVAL);
+  EXPECT(zero_adam_derive_table(&hp, 1, NULL) == ZERO_E_INVAL);
+  hp.beta2 = -1.0;
+  EXPECT(zero_adam_derive_table(&hp, count, tab) == ZERO_E_INVAL);
+  delete[] tab;
 }
 
 static void host_updates() {

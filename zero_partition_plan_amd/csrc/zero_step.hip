@@ -81,7 +81,8 @@ __device__ __forceinline__ void dev_scalars(const DevCtl& dc, StepScalars& sc) {
   sc.gs = *dc.gs;
   if (dc.table != nullptr) {
     const int64_t t = *dc.step;
-    const uint32_t i = t < 1 ? 0u : (t >= (int64_t)dc.table_len ? dc.table_len - 1u : (uint32_t)(t - 1));
+    const uint32_t i =
+        t < 1 ? 0u : (t >= (int64_t)dc.table_len ? dc.table_len - 1u : (uint32_t)(t - 1));
     const zero_adam_scalars k = dc.table[i];
     sc.b1 = k.b1;
     sc.b2 = k.b2;

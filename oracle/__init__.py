@@ -26,8 +26,8 @@ Modules:
   memory     per-stage model-state bytes per rank (DP, ZeRO-1/2/3), the bytes a
              rank sends per step under each stage, and the stage-choice rule  [P1 一/二/三/四; P3 stages]
 
-Parity status of each function is stated in its docstring; the clip-coefficient formula is
-"parity unpinned" (no page defines it).
+Parity status of each function is stated in its docstring. The clip coefficient has no page; its
+reading is pinned against torch.nn.utils.clip_grad_norm_, a library implementation of the rule.
 """
 
 from .partition import Plan, partition_plan, shard_range

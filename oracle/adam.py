@@ -17,8 +17,9 @@ scaling, overflow or clipping):
     ``adam_update``) so that another implementation can reproduce it bit for bit.
   * overflow: the whole step is skipped when any summed gradient element is not finite.
   * squared norm: sum over the shard of (acc_i * sq_scale)^2 with fp64 terms, padding included.
-  * clip coefficient: min(1, max_norm / (sqrt(total_sq) + 1e-6)) in fp64 ("parity unpinned": no
-    page defines it; only its limits are pinned).
+  * clip coefficient: min(1, max_norm / (sqrt(total_sq) + 1e-6)) in fp64. No page defines it; the
+    reading is the usual global-norm rule, pinned against torch.nn.utils.clip_grad_norm_ (which
+    forms its own norm and coefficient) in the tests.
 """
 
 from __future__ import annotations
@@ -124,8 +125,10 @@ def shard_sqnorm(acc: np.ndarray, sq_scale: float = 1.0, chunk: int = 1 << 20) -
 
 def clip_coefficient(total_sq: float, max_norm: float = 1.0, eps: float = 1e-6) -> float:
     """min(1, max_norm / (||g|| + eps)) in IEEE fp64: a zero norm with eps = 0 divides to +inf
-    (coefficient 1), an infinite norm gives 0, and a NaN quotient gives 1. Parity unpinned (no page
-    defines clipping)."""
+    (coefficient 1), an infinite norm gives 0, and a NaN quotient gives 1. No page defines
+    clipping; this is the global-norm rule read for the clipped step, pinned against
+    torch.nn.utils.clip_grad_norm_ on fp64 gradients (exact norms below, at and above max_norm,
+    tiny and huge norms, random gradients) and by planted mistakes that those pins catch."""
     with np.errstate(divide="ignore", invalid="ignore"):
         q = float(np.float64(max_norm) / (np.sqrt(np.float64(total_sq)) + np.float64(eps)))
     return min(1.0, q)

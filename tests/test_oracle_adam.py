@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import oracle as O
+import clip_pins as CP
 import adam_pins as P
 from workloads import WORKLOADS
 from workloads import host as H
@@ -93,12 +94,7 @@ def test_sqnorm_closed_forms():
     assert O.shard_sqnorm(a, 2.0 ** -16) == 12345 * 0.5625 * 2.0 ** -32
 
 
-def test_clip_coefficient_limits():
-    # parity unpinned as a formula; only its limits are pinned
-    assert O.clip_coefficient(0.25, max_norm=1.0) == 1.0
-    assert O.clip_coefficient(0.0) == 1.0
-    c = O.clip_coefficient(100.0, max_norm=1.0)
-    assert c == pytest.approx(0.1, rel=1e-6) and c < 0.1
+def test_clip_coefficient_ieee_edges():
     # IEEE edges: a zero norm with eps = 0 is not clipped, an infinite norm scales to 0, NaN gives 1
     assert O.clip_coefficient(0.0, max_norm=1.0, eps=0.0) == 1.0
     assert O.clip_coefficient(float("inf")) == 0.0
@@ -106,6 +102,13 @@ def test_clip_coefficient_limits():
     # with eps = 0 and a perfect-square norm the quotient is exact
     assert O.clip_coefficient(16.0, max_norm=1.0, eps=0.0) == 0.25
     assert O.clip_coefficient(2.0 ** -40, max_norm=2.0 ** -30, eps=0.0) == 2.0 ** -10
+
+
+@pytest.mark.parametrize("check", sorted(CP.ALL_CHECKS))
+def test_clip_coefficient_against_torch(check):
+    """The clip rule against torch.nn.utils.clip_grad_norm_ (fp64 CPU gradients): exact norms
+    below, at and above max_norm, tiny and huge norms, several tensors, random gradients."""
+    CP.ALL_CHECKS[check]()
 
 
 def test_union_of_shards_equals_unsharded_tiny():

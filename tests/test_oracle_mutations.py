@@ -12,6 +12,7 @@ import pytest
 
 import oracle as O
 import adam_pins as P
+import clip_pins as CP
 
 
 def _scalars_with(**over):
@@ -103,3 +104,36 @@ def test_sum_mutants_are_caught():
     assert rev[0] != O.replica_sum(a, "f32")[0] or mean[0] != 0.0
     k = np.arange(-8, 8, dtype=np.float32).reshape(4, 4) * np.float32(0.25)
     assert not np.array_equal(O.replica_sum(list(k), "f32") / np.float32(4), k.sum(0))
+
+
+def _clip_variant(kind):
+    """Plausible mistakes in the clip rule min(1, max_norm / (sqrt(sq) + eps))."""
+    def clip(total_sq, max_norm=1.0, eps=1e-6):
+        if kind == "eps_inside_sqrt":
+            q = max_norm / math.sqrt(total_sq + eps)
+        elif kind == "eps_dropped":
+            q = max_norm / math.sqrt(total_sq) if total_sq > 0 else math.inf
+        elif kind == "squared_norm_as_norm":
+            q = max_norm / (total_sq + eps)
+        else:
+            q = max_norm / (math.sqrt(total_sq) + eps)
+        return max(1.0, q) if kind == "max_for_min" else min(1.0, q)
+    return clip
+
+
+@pytest.mark.parametrize("kind", ["eps_inside_sqrt", "eps_dropped", "squared_norm_as_norm", "max_for_min"])
+def test_clip_mutant_is_caught(kind):
+    caught = []
+    for check_name, check in CP.ALL_CHECKS.items():
+        try:
+            check(_clip_variant(kind))
+        except AssertionError:
+            caught.append(check_name)
+    assert caught, f"clip mutant {kind} passed every pin"
+
+
+def test_clip_unmutated_variant_passes():
+    """The mutants' own scaffold, unmutated, passes every pin (so a caught mutant is caught for its
+    mistake, not for the scaffold)."""
+    for check in CP.ALL_CHECKS.values():
+        check(_clip_variant("none"))

@@ -52,8 +52,8 @@ HBM_PEAK_GBS = 8000.0
 _CSRC = os.path.join(ROOT, "zero_partition_plan_amd", "csrc")
 # the device sources each kernel is built from
 KERNEL_SRCS = {k: [os.path.join(_CSRC, f) for f in fs] for k, fs in {
-    "k_adam_step": ("zero_step.hip", "zero_device.h"),
-    "k_reduce": ("zero_step.hip", "zero_device.h"),
+    "k_adam_step": ("zero_step_kernels.hip", "zero_step.h", "zero_device.h"),
+    "k_reduce": ("zero_step_kernels.hip", "zero_step.h", "zero_device.h"),
     "k_gather": ("zero_gather.hip", "zero_device.h"),
 }.items()}
 PROFILES = os.path.join(ROOT, "profiles")
@@ -567,9 +567,10 @@ def graph_steps(st, steps=50):
     table = Z.adam_table(hp, st["t"] + 2 * steps + 8)
     gs = torch.ones(1, device="cuda")
     t_dev = torch.full((1,), st["t"], dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     def one():
-        Z.zero_adam_shard_step_dev_t(inp["reps"], S, gs, table, t_dev, inp["master"], inp["m"],
+        Z.zero_adam_shard_step_dev_t(inp["reps"], S, gs, table, t_dev, status, inp["master"], inp["m"],
                                      inp["v"], wd_mode=w.wd_mode, out=st["slot"])
 
     side = torch.cuda.Stream()
@@ -588,6 +589,7 @@ def graph_steps(st, steps=50):
     e1.record()
     torch.cuda.synchronize()
     graph_ms = e0.elapsed_time(e1) / steps
+    assert int(status.item()) == 0, "a replayed step ran past its constants table"
     st["t"] = int(t_dev.item())
     eager = Spans(False)
     step_fused(st, eager)

@@ -17,7 +17,7 @@
  *     pointers must be device memory of the current HIP device; everything else is host memory.
  *   - Ownership: the caller allocates and frees every buffer. No entry point allocates memory except
  *     zero_arena_alloc, which exists to be asked for it; the library keeps no state except a
- *     thread-local error message and a per-device launch-size cache.
+ *     thread-local error message.
  *   - Streams: device work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and
  *     never synchronised, except where an entry point says otherwise; device outputs are valid once
  *     the stream reaches that point.
@@ -215,7 +215,10 @@ uint64_t zero_sq_partials_len(uint64_t n);
  *                 sum over i in [256t, 256t+256) of (double(acc[i]) * sq_scale)^2, each in a fixed
  *                 order that does not depend on alignment; finish with zero_shard_sqnorm(NULL, n).
  * n == 0 enqueues nothing. Aliasing: out_grad and d_sq_partials must not overlap a replica or each
- * other. Errors: bad source, no output, aliasing -> ZERO_E_INVAL; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
+ * other, and d_nonfinite must not lie in a replica, out_grad or the partials. Alignment: every
+ * array naturally aligned (fp32 and the flag on 4 bytes, 16-bit on 2, the partials on 8), at any
+ * element offset; all take the vector path. Errors: bad source, no output, aliasing, an array not
+ * naturally aligned -> ZERO_E_INVAL; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
 zero_status zero_reduce_shard(const zero_grad_src* src, uint64_t n, float* out_grad,
                               int32_t* d_nonfinite, double* d_sq_partials, double sq_scale,
                               void* stream);
@@ -227,7 +230,7 @@ zero_status zero_reduce_shard(const zero_grad_src* src, uint64_t n, float* out_g
  * chunks of ceil(tiles/1024) partials, then the chunk sums), using the buffer's last 1024 slots as
  * scratch, and writes the result to *d_out (device double; 0 for n == 0). d_partials holds
  * zero_sq_partials_len(n) doubles. Errors: d_partials or d_out NULL, d_out inside the partials or
- * the gradient -> ZERO_E_INVAL; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
+ * the gradient, an array not naturally aligned -> ZERO_E_INVAL; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
 zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, double* d_partials,
                               double* d_out, void* stream);
 
@@ -245,10 +248,12 @@ zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, 
  * (ZERO_BF16 or ZERO_F16); pass the full gathered buffer plus r*S to write rank r's slot.
  * d_skip (device int32, nullable): when it holds a non-zero value at kernel start, nothing is
  * written (the overflow-skip path: the caller then does not advance t).
- * Aliasing: master, m, v, out_param must not overlap each other or any replica.
- * Any alignment is accepted; 16-byte-aligned arrays take the vector path.
- * Errors: NULLs, bad source, bad hparams, aliasing -> ZERO_E_INVAL; out_dtype ZERO_F32 ->
- * ZERO_E_UNSUPPORTED; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
+ * Aliasing: master, m, v, out_param must not overlap each other, any replica or d_skip.
+ * Alignment: every array naturally aligned (fp32 and d_skip on 4 bytes, 16-bit on 2), at any
+ * element offset: a slot at an odd element r*S of the gathered buffer (odd S) or replicas that are
+ * slices of full-length gradient buffers take the same vector path as aligned ones.
+ * Errors: NULLs, bad source, bad hparams, aliasing, an array not naturally aligned ->
+ * ZERO_E_INVAL; out_dtype ZERO_F32 -> ZERO_E_UNSUPPORTED; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
 zero_status zero_adam_shard_step(const zero_grad_src* src, uint64_t n, float grad_scale,
                                  float* master, float* m, float* v, const zero_adam_hparams* hp,
                                  void* out_param, int32_t out_dtype, const int32_t* d_skip,
@@ -266,23 +271,31 @@ zero_status zero_adam_shard_step_dev_scale(const zero_grad_src* src, uint64_t n,
                                            float* v, const zero_adam_hparams* hp, void* out_param,
                                            int32_t out_dtype, const int32_t* d_skip, void* stream);
 
+/* Device status word of zero_adam_shard_step_dev_t: the device step t lay outside its constants
+ * table, so the update wrote nothing and t did not advance. */
+#define ZERO_DEV_T_OUT_OF_TABLE 1
+
 /* The step of zero_adam_shard_step (P1 section 二; P2 ZeRO Stage 1/2) with its step counter also in
  * device memory, so that a whole training step can be enqueued, or captured in a graph and
- * replayed, without the host supplying t: each update block reads t = *d_step (device int64,
- * t >= 1) and takes its constants from d_table[t-1] (device zero_adam_scalars[table_len], e.g.
- * zero_adam_derive_table's; a t past the table takes its last entry, a t below 1 its first), and
- * the grad scale from *d_grad_scale. After the update one
- * single-thread kernel on the same stream advances *d_step by one unless d_skip is set (a skipped
- * step does not count). With n == 0 only that advance is enqueued. wd_mode is the zero_wd_mode the
- * table was derived for. Everything else as zero_adam_shard_step.
- * Errors: as zero_adam_shard_step; NULL d_grad_scale, d_table or d_step, table_len == 0, an
- * unknown wd_mode, d_step overlapping the table, the grad scale or the flag, or master, m, v or
- * out_param overlapping any of them -> ZERO_E_INVAL. */
+ * replayed, without the host supplying t: each update block reads t = *d_step (device int64) and
+ * takes its constants from d_table[t-1] (device zero_adam_scalars[table_len], e.g.
+ * zero_adam_derive_table's) and the grad scale from *d_grad_scale. A t outside [1, table_len] has
+ * no constants: then nothing is written (master, m, v and out_param keep their bits), t does not
+ * advance and *d_status (device int32, zeroed by the caller; only ever set, so one check covers
+ * many calls or graph replays) receives ZERO_DEV_T_OUT_OF_TABLE. After the update one
+ * single-thread kernel on the same stream does that report, or advances *d_step by one, unless
+ * d_skip is set (a skipped step does not count). With n == 0 only that kernel is enqueued. wd_mode
+ * is the zero_wd_mode the table was derived for. Everything else as zero_adam_shard_step.
+ * Errors: as zero_adam_shard_step; NULL d_grad_scale, d_table, d_step or d_status, table_len == 0,
+ * an unknown wd_mode, d_step overlapping the table, the grad scale, the flag or a replica, d_status
+ * overlapping any array or word of the call, or master, m, v or out_param overlapping any of them
+ * -> ZERO_E_INVAL. */
 zero_status zero_adam_shard_step_dev_t(const zero_grad_src* src, uint64_t n,
                                        const float* d_grad_scale, const zero_adam_scalars* d_table,
-                                       uint32_t table_len, int64_t* d_step, int32_t wd_mode,
-                                       float* master, float* m, float* v, void* out_param,
-                                       int32_t out_dtype, const int32_t* d_skip, void* stream);
+                                       uint32_t table_len, int64_t* d_step, int32_t* d_status,
+                                       int32_t wd_mode, float* master, float* m, float* v,
+                                       void* out_param, int32_t out_dtype, const int32_t* d_skip,
+                                       void* stream);
 
 /* Gradient-clipping scale for the two-pass step, formed on the device. The pages do not clip; this
  * is the usual global-norm rule, with the shard's squared norm standing for the global one:

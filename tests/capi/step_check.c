@@ -160,18 +160,26 @@ int main(void) {
       zero_adam_scalars table[8];
       zero_adam_scalars* d_table;
       int64_t t = hp.step, *d_t;
+      int32_t status = -1, *d_status;
       ZS(zero_adam_derive_table(&hp, 8, table));
       HIP(hipMalloc((void**)&d_table, sizeof table));
       HIP(hipMalloc((void**)&d_t, 8));
+      HIP(hipMalloc((void**)&d_status, 4));
+      HIP(hipMemset(d_status, 0, 4));
       HIP(hipMemcpy(d_table, table, sizeof table, hipMemcpyHostToDevice));
       HIP(hipMemcpy(d_t, &t, 8, hipMemcpyHostToDevice));
       HIP(hipMemcpy(d_p, p0, N * 4, hipMemcpyHostToDevice));
       HIP(hipMemcpy(d_m, m0, N * 4, hipMemcpyHostToDevice));
       HIP(hipMemcpy(d_v, v0, N * 4, hipMemcpyHostToDevice));
-      ZS(zero_adam_shard_step_dev_t(&src, N, d_gs, d_table, 8, d_t, ZERO_ADAMW, d_p, d_m, d_v,
-                                    d_out, ZERO_BF16, NULL, NULL));
+      ZS(zero_adam_shard_step_dev_t(&src, N, d_gs, d_table, 8, d_t, d_status, ZERO_ADAMW, d_p, d_m,
+                                    d_v, d_out, ZERO_BF16, NULL, NULL));
       HIP(hipDeviceSynchronize());
       HIP(hipMemcpy(&t, d_t, 8, hipMemcpyDeviceToHost));
+      HIP(hipMemcpy(&status, d_status, 4, hipMemcpyDeviceToHost));
+      if (status != 0) {
+        fprintf(stderr, "status word %d after a step inside the table\n", (int)status);
+        ++bad;
+      }
       HIP(hipMemcpy(p_dev, d_p, N * 4, hipMemcpyDeviceToHost));
       HIP(hipMemcpy(m_dev, d_m, N * 4, hipMemcpyDeviceToHost));
       HIP(hipMemcpy(v_dev, d_v, N * 4, hipMemcpyDeviceToHost));
@@ -190,6 +198,7 @@ int main(void) {
       }
       HIP(hipFree(d_table));
       HIP(hipFree(d_t));
+      HIP(hipFree(d_status));
     }
     HIP(hipFree(d_parts));
     HIP(hipFree(d_sq));

@@ -255,28 +255,71 @@ def test_device_step_entry_point_validates_first():
     fake = 1 << 40                                   # never dereferenced: every call below is invalid
     ok_src, k1 = _src([fake])
     step = L.zero_adam_shard_step_dev_t
-    gs, tab, t = fake + 100000, fake + 200000, fake + 300000
+    gs, tab, t, st = fake + 100000, fake + 200000, fake + 300000, fake + 400000
     P, M, V = fake + 4096, fake + 8192, fake + 12288
-    # NULL grad scale / table / step, empty table, unknown wd_mode (even for n = 0)
-    assert step(ctypes.byref(ok_src), 0, None, tab, 4, t, 0, None, None, None, None, 0, None, None) == 1
-    assert step(ctypes.byref(ok_src), 0, gs, None, 4, t, 0, None, None, None, None, 0, None, None) == 1
-    assert step(ctypes.byref(ok_src), 0, gs, tab, 4, None, 0, None, None, None, None, 0, None, None) == 1
-    assert step(ctypes.byref(ok_src), 0, gs, tab, 0, t, 0, None, None, None, None, 0, None, None) == 1
-    assert step(ctypes.byref(ok_src), 0, gs, tab, 4, t, 9, None, None, None, None, 0, None, None) == 1
-    # the step inside the table, on the grad scale or on the flag
-    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, tab + 36, 0, P, M, V, None, 0, None, None) == 1
-    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, gs, 0, P, M, V, None, 0, None, None) == 1
-    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, P, M, V, None, 0, t + 4, None) == 1
+
+    def call(n, gs_, tab_, len_, t_, st_, mode, p, m, v, out=None, odt=0, skip=None):
+        return step(ctypes.byref(ok_src), n, gs_, tab_, len_, t_, st_, mode, p, m, v, out, odt, skip, None)
+
+    # NULL grad scale / table / step / status, empty table, unknown wd_mode (even for n = 0)
+    assert call(0, None, tab, 4, t, st, 0, None, None, None) == 1
+    assert call(0, gs, None, 4, t, st, 0, None, None, None) == 1
+    assert call(0, gs, tab, 4, None, st, 0, None, None, None) == 1
+    assert call(0, gs, tab, 4, t, None, 0, None, None, None) == 1
+    assert "d_status" in Z.zero_last_error()
+    assert call(0, gs, tab, 0, t, st, 0, None, None, None) == 1
+    assert call(0, gs, tab, 4, t, st, 9, None, None, None) == 1
+    # the step inside the table, on the grad scale, on the flag or inside a replica
+    assert call(100, gs, tab, 4, tab + 36, st, 0, P, M, V) == 1
+    assert call(100, gs, tab, 4, gs, st, 0, P, M, V) == 1
+    assert call(100, gs, tab, 4, t, st, 0, P, M, V, skip=t + 4) == 1
     assert "d_step overlaps" in Z.zero_last_error()
-    # an output array over the table, the step or the grad scale
-    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, tab - 8, M, V, None, 0, None, None) == 1
+    assert call(100, gs, tab, 4, fake + 64, st, 0, P, M, V) == 1
+    assert "d_step overlaps replica 0" in Z.zero_last_error()
+    # the status word inside any array or word of the call
+    for where, what in ((P + 8, "master"), (M, "m"), (V + 396, "v"), (tab + 4, "constants table"),
+                        (gs, "grad scale"), (t + 4, "the step"), (fake + 10, "replica 0")):
+        assert call(100, gs, tab, 4, t, where, 0, P, M, V) == 1, what
+        assert "d_status overlaps" in Z.zero_last_error() and what in Z.zero_last_error(), what
+    assert call(100, gs, tab, 4, t, fake + 20000, 0, P, M, V, out=fake + 20000 - 8, odt=Z.ZERO_BF16) == 1
+    assert "d_status overlaps out_param" in Z.zero_last_error()
+    assert call(100, gs, tab, 4, t, fake + 30000, 0, P, M, V, skip=fake + 30000) == 1
+    assert "d_status overlaps the skip flag" in Z.zero_last_error()
+    # an output array over the table, the step, the grad scale or the skip flag
+    assert call(100, gs, tab, 4, t, st, 0, tab - 8, M, V) == 1
     assert "constants table" in Z.zero_last_error()
-    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, P, t - 4, V, None, 0, None, None) == 1
-    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, P, M, V, gs - 2, Z.ZERO_BF16, None, None) == 1
+    assert call(100, gs, tab, 4, t, st, 0, P, t - 4, V) == 1
+    assert call(100, gs, tab, 4, t, st, 0, P, M, V, out=gs - 2, odt=Z.ZERO_BF16) == 1
+    assert call(100, gs, tab, 4, t, st, 0, P, M, V, skip=V + 40) == 1
+    assert "skip flag" in Z.zero_last_error()
     # zero_adam_shard_step's own checks still apply
-    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, None, M, V, None, 0, None, None) == 1
-    assert step(ctypes.byref(ok_src), 100, gs, tab, 4, t, 0, P, M, V, fake + 16384, Z.ZERO_F32, None, None) == 3
-    assert step(ctypes.byref(ok_src), 1 << 62, gs, tab, 4, t, 0, P, M, V, None, 0, None, None) == 2
+    assert call(100, gs, tab, 4, t, st, 0, None, M, V) == 1
+    assert call(100, gs, tab, 4, t, st, 0, P, M, V, out=fake + 16384, odt=Z.ZERO_F32) == 3
+    assert call(1 << 62, gs, tab, 4, t, st, 0, P, M, V) == 2
+
+
+def test_flag_words_must_not_alias_arrays():
+    """A flag the kernels read (skip) or write (non-finite) lying inside an array the same call
+    writes, or a written flag inside a replica, would change under the blocks that start later:
+    each such placement is refused before any launch."""
+    L = Z.lib()
+    fake = 1 << 40                                   # never dereferenced: every call below is invalid
+    hp = Z.adam_hparams()
+    src, keep = _src([fake, fake + 8192], Z.ZERO_BF16)
+    P, M, V, O = fake + (1 << 20), fake + (2 << 20), fake + (3 << 20), fake + (4 << 20)
+    n = 1000
+    for skip, what in ((P + 12, "master"), (M, "m"), (V + 3996, "v"), (O + 100, "out_param")):
+        assert L.zero_adam_shard_step(ctypes.byref(src), n, 1.0, P, M, V, ctypes.byref(hp), O,
+                                      Z.ZERO_BF16, skip, None) == 1, what
+        assert "skip flag" in Z.zero_last_error() and what in Z.zero_last_error(), what
+    # a skip flag next to the arrays (not inside) is fine up to the launch: n = 0 launches nothing
+    assert L.zero_adam_shard_step(ctypes.byref(src), 0, 1.0, P, M, V, ctypes.byref(hp), O,
+                                  Z.ZERO_BF16, P - 4, None) == 0
+    G, parts = fake + (5 << 20), fake + (6 << 20)
+    for flag, what in ((fake + 100, "replica 0"), (fake + 8192 + 1996, "replica 1"), (G + 8, "out_grad"),
+                       (parts + 16, "the partials")):
+        assert L.zero_reduce_shard(ctypes.byref(src), n, G, flag, parts, 1.0, None) == 1, what
+        assert "d_nonfinite overlaps" in Z.zero_last_error() and what in Z.zero_last_error(), what
 
 
 def test_sq_partials_len():
@@ -439,3 +482,29 @@ def test_error_messages_are_per_thread():
     for t in threads:
         t.join()
     assert all(v == {True} for v in results.values()), results
+
+
+def test_arrays_off_natural_alignment_are_refused():
+    """Any element offset is accepted, but an array must be aligned to its own element size (the
+    hardware drops the low address bits of word-sized accesses): a float pointer one byte off, or a
+    16-bit one an odd byte off, is refused before any launch."""
+    L = Z.lib()
+    fake = 1 << 40                                   # never dereferenced: every call below is invalid
+    hp = Z.adam_hparams()
+    P, M, V, O = fake + (1 << 20), fake + (2 << 20), fake + (3 << 20), fake + (4 << 20)
+    good16, k1 = _src([fake + 2, fake + 8194], Z.ZERO_BF16)     # odd elements: fine
+    bad16, k2 = _src([fake, fake + 8193], Z.ZERO_BF16)
+    bad32, k3 = _src([fake + 6], Z.ZERO_F32)
+    n = 1000
+    for src, args, what in ((bad16, (P, M, V, O), "replica 1"), (bad32, (P, M, V, O), "replica 0"),
+                            (good16, (P + 1, M, V, O), "master"), (good16, (P, M + 2, V, O), "master"),
+                            (good16, (P, M, V + 3, O), "master"), (good16, (P, M, V, O + 1), "master")):
+        assert L.zero_adam_shard_step(ctypes.byref(src), n, 1.0, *args[:3], ctypes.byref(hp), args[3],
+                                      Z.ZERO_BF16, None, None) == 1, what
+        assert "not aligned" in Z.zero_last_error(), what
+    G, parts = fake + (5 << 20), fake + (6 << 20)
+    assert L.zero_reduce_shard(ctypes.byref(bad16), n, G, None, None, 1.0, None) == 1
+    assert L.zero_reduce_shard(ctypes.byref(good16), n, G + 2, None, None, 1.0, None) == 1
+    assert L.zero_reduce_shard(ctypes.byref(good16), n, None, None, parts + 4, 1.0, None) == 1
+    assert L.zero_shard_sqnorm(G + 1, n, 1.0, parts, parts - 8, None) == 1
+    assert "not aligned" in Z.zero_last_error()

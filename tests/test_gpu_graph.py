@@ -132,6 +132,7 @@ def test_clipped_step_with_device_counter_replays_as_successive_steps():
                     sq=torch.empty(1, dtype=torch.float64, device=DEV),
                     gs=torch.empty(1, dtype=torch.float32, device=DEV),
                     t=torch.ones(1, dtype=torch.int64, device=DEV),
+                    status=torch.zeros(1, dtype=torch.int32, device=DEV),
                     out=torch.zeros(n, dtype=torch.float16, device=DEV))
 
     def front(b):
@@ -142,8 +143,8 @@ def test_clipped_step_with_device_counter_replays_as_successive_steps():
 
     def graph_step(b):
         front(b)
-        Z.zero_adam_shard_step_dev_t([b["g"]], n, b["gs"], table, b["t"], b["p"], b["m"], b["v"],
-                                     out=b["out"], skip=b["flag"])
+        Z.zero_adam_shard_step_dev_t([b["g"]], n, b["gs"], table, b["t"], b["status"], b["p"], b["m"],
+                                     b["v"], out=b["out"], skip=b["flag"])
 
     gb, eb = buffers(), buffers()
     side = torch.cuda.Stream()
@@ -177,4 +178,4 @@ def test_clipped_step_with_device_counter_replays_as_successive_steps():
             assert torch.equal(a.view(torch.int16 if a.element_size() == 2 else torch.int32),
                                b.view(torch.int16 if b.element_size() == 2 else torch.int32)), (k, key)
         assert gb["gs"].view(torch.int32).item() == eb["gs"].view(torch.int32).item(), k
-    assert t_host == 5
+    assert t_host == 5 and int(gb["status"].item()) == 0

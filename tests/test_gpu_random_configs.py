@@ -6,7 +6,9 @@ dtype, either output dtype or none, both decay modes, a random grad scale and st
 element offsets (so the vector path, the per-element path and the partial last tile all occur) and
 the skip flag; odd seeds pass the grad scale in device memory (zero_adam_shard_step_dev_scale),
 and every fourth seed also the step, with constants tables of 1, 7 or 2500 entries
-(zero_adam_shard_step_dev_t).
+(zero_adam_shard_step_dev_t: a step past its table must write nothing and set the status word).
+Odd element offsets put 16-bit arrays 2 bytes past a 4-byte word, and any offset puts fp32 arrays
+off 16 bytes, so the word-realigning vector path is drawn often.
 Gather cases draw shard counts and sizes, ranges, element sizes and source and
 output offsets. Every fp32 and 16-bit result is compared bit for bit, the squared norm to 1e-10.
 """
@@ -80,14 +82,16 @@ def test_random_fused_step(seed):
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=c["wd"], wd_mode=c["mode"],
               step=c["step"])
     d_t = None
+    refused = False
     if seed % 4 == 3:                  # the grad scale and the step from device memory
         d_gs = torch.full((1,), c["gs"], dtype=torch.float32, device=DEV)
-        table_len = [1, 7, 2500][seed // 4 % 3]      # shorter tables clamp t to their last entry
+        table_len = [1, 7, 2500][seed // 4 % 3]      # shorter tables have no constants for t
         table = Z.adam_table(Z.adam_hparams(**hp), table_len, device=DEV)
         d_t = torch.full((1,), c["step"], dtype=torch.int64, device=DEV)
-        Z.zero_adam_shard_step_dev_t(d_reps, n, d_gs, table, d_t, d_p, d_m, d_v, wd_mode=c["mode"],
-                                     out=d_out, skip=skip)
-        hp["step"] = min(c["step"], table_len)
+        d_status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        Z.zero_adam_shard_step_dev_t(d_reps, n, d_gs, table, d_t, d_status, d_p, d_m, d_v,
+                                     wd_mode=c["mode"], out=d_out, skip=skip)
+        refused = c["step"] > table_len and c["skip"] != 1
     elif seed % 2:                     # the grad scale read from device memory
         d_gs = torch.full((1,), c["gs"], dtype=torch.float32, device=DEV)
         Z.zero_adam_shard_step_dev_scale(d_reps, n, d_gs, d_p, d_m, d_v, Z.adam_hparams(**hp),
@@ -97,8 +101,9 @@ def test_random_fused_step(seed):
                                skip=skip)
     torch.cuda.synchronize()
     if d_t is not None:
-        assert int(d_t.item()) == c["step"] + (0 if c["skip"] == 1 else 1)
-    skipped = c["skip"] == 1
+        assert int(d_t.item()) == c["step"] + (0 if c["skip"] == 1 or refused else 1)
+        assert int(d_status.item()) == (Z.ZERO_DEV_T_OUT_OF_TABLE if refused else 0)
+    skipped = c["skip"] == 1 or refused       # a refused update writes nothing, as a skipped one
     wp, wm, wv, wo = O.sharded_step(list(reps), c["rdt"], c["gs"], p, m, v, O.AdamHParams(**hp),
                                     c["odt"], skip=skipped)
     assert_bits_equal(bits32(d_p), f32_bits(wp), "master")

@@ -105,6 +105,68 @@ def test_step_misaligned_arrays(offsets):
     _check_step(_reps_np(rng, 3, n, "bf16"), "bf16", n, HP, "bf16", rng, offsets=offsets)
 
 
+@pytest.mark.parametrize("rdt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("R", [5, 8, 16, 64])
+@pytest.mark.parametrize("out_off", [0, 1, 2, 3])
+def test_step_replica_and_slot_phases(rdt, R, out_off):
+    """Replica k placed k elements into its buffer (16-bit replicas then alternate between starting
+    on a 4-byte word and 2 bytes past one), master/m/v 1, 2 and 3 elements in (off 16 bytes), and
+    the 16-bit slot at each offset mod 4, over several tiles and a ragged tail: every result bit for
+    bit against the oracle, and no byte written outside the slot (its first and last elements sit
+    next to the canaries)."""
+    n = 9 * TILE + 77
+    banner(f"step phases rdt={rdt} R={R} out_off={out_off}")
+    rng = np.random.default_rng(1000 * R + out_off)
+    reps = _reps_np(rng, R, n, rdt)
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (rng.random(n) * 1e-7).astype(np.float32)
+    d_reps = [dev_rep(np.concatenate([np.zeros(k % 4, r.dtype), r]), rdt)[k % 4:] for k, r in enumerate(reps)]
+    d_p = dev_f32(np.concatenate([np.zeros(1, np.float32), master]))[1:]
+    d_m = dev_f32(np.concatenate([np.zeros(2, np.float32), m]))[2:]
+    d_v = dev_f32(np.concatenate([np.zeros(3, np.float32), v]))[3:]
+    for odt in ("bf16", "f16"):
+        p, mm, vv = d_p.clone(), d_m.clone(), d_v.clone()
+        full = empty16(n + out_off + 5, odt, fill=-3.0)
+        Z.zero_adam_shard_step(d_reps, n, 0.5, p, mm, vv, Z.adam_hparams(**HP), out=full[out_off:out_off + n])
+        torch.cuda.synchronize()
+        wp, wm, wv, wo = O.sharded_step(list(reps), rdt, 0.5, master, m, v, O.AdamHParams(**HP), odt)
+        assert_bits_equal(bits32(p), f32_bits(wp), f"{odt} master")
+        assert_bits_equal(bits32(mm), f32_bits(wm), f"{odt} m")
+        assert_bits_equal(bits32(vv), f32_bits(wv), f"{odt} v")
+        got = bits16(full)
+        canary = (O.cast_bf16_rne if odt == "bf16" else O.cast_fp16_rne)(np.float32([-3.0]))[0]
+        assert (got[:out_off] == canary).all() and (got[out_off + n:] == canary).all(), "write outside the slot"
+        assert_bits_equal(got[out_off:out_off + n], wo, f"{odt} slot")
+
+
+@pytest.mark.parametrize("rdt", ["bf16", "f16"])
+@pytest.mark.parametrize("R", [3, 16, 64])
+def test_reduce_replica_phases(rdt, R):
+    """The reduce pass with replicas at mixed phases (replica k, k elements into its buffer) and the
+    gradient 1 element in: gradient, flag and every per-tile partial bit-equal to the same pass on
+    aligned copies, and the gradient bit-equal to the oracle."""
+    n = 11 * TILE + 45
+    banner(f"reduce phases rdt={rdt} R={R}")
+    rng = np.random.default_rng(77 + R)
+    reps = _reps_np(rng, R, n, rdt)
+    runs = []
+    for shifted in (False, True):
+        d_reps = [dev_rep(np.concatenate([np.zeros(k % 4 if shifted else 0, r.dtype), r]), rdt)[(k % 4 if shifted else 0):]
+                  for k, r in enumerate(reps)]
+        g_buf = torch.empty(n + 1, device=DEV)
+        g = g_buf[1:] if shifted else g_buf[:n]
+        flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+        parts = torch.empty(Z.zero_sq_partials_len(n), dtype=torch.float64, device=DEV)
+        Z.zero_reduce_shard(d_reps, n, g, flag, parts, 2.0 ** -6)
+        torch.cuda.synchronize()
+        runs.append((bits32(g), int(flag.item()), parts.cpu().numpy()[:math.ceil(n / TILE)].copy()))
+    assert_bits_equal(runs[1][0], runs[0][0], "gradient")
+    assert runs[0][1] == runs[1][1] == 0
+    assert np.array_equal(runs[0][2], runs[1][2])
+    assert_bits_equal(runs[0][0], f32_bits(O.replica_sum(list(reps), rdt)), "gradient vs oracle")
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 1023, TILE - 1, TILE, TILE + 1])
 def test_step_small_and_edge_sizes(n):
     banner(f"step n={n}")
@@ -267,9 +329,8 @@ def test_reduce_matches_oracle(dtype, R):
 
 @pytest.mark.parametrize("n", [1, 5, TILE - 1, TILE + 3, 20000 * TILE + 17])
 def test_reduce_sizes_and_misalignment(n):
-    """Aligned arrays take the vector path for whole tiles, a replica one element off takes the
-    per-element path everywhere; the gradient, the per-tile partials and the norm must agree bit
-    for bit between the two (the element order inside a tile does not depend on the path)."""
+    """A replica on a 4-byte word and one 2 bytes past it (the word-realigning loads): the
+    gradient, the per-tile partials and the norm must agree bit for bit between the two."""
     banner(f"reduce n={n}")
     rng = np.random.default_rng(n % 1000)
     reps = _reps_np(rng, 2, n, "bf16")
@@ -461,9 +522,10 @@ def test_device_scale_step_equals_host_scale_step():
 
 
 def test_device_step_counter_equals_host_steps():
-    """zero_adam_shard_step_dev_t over five steps (t, constants and grad scale read on the device,
-    t advanced on the device) gives the bits of the same steps with t from the host; a skipped step
-    leaves the state and t alone; a t past the table takes its last entry; n = 0 only advances t."""
+    """zero_adam_shard_step_dev_t over steps t = 3..6 (t, constants and grad scale read on the
+    device, t advanced on the device) gives the bits of the same steps with t from the host; a
+    skipped step leaves the state and t alone; t = 7, past the 6-entry table, writes nothing, keeps
+    t and sets the status word; n = 0 only runs the counter kernel."""
     n, R, t0 = 7 * TILE + 45, 8, 3
     rng = np.random.default_rng(17)
     reps = [dev_rep(r, "bf16") for r in _reps_np(rng, R, n, "bf16")]
@@ -474,28 +536,72 @@ def test_device_step_counter_equals_host_steps():
     host = [t.clone() for t in dev]
     d_out, h_out = empty16(n, "bf16"), empty16(n, "bf16")
     step = torch.full((1,), t0, dtype=torch.int64, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
     gs = torch.full((1,), 0.75, device=DEV)
     skip = torch.zeros(1, dtype=torch.int32, device=DEV)
     t_host = t0
-    for k, skipped in enumerate((False, False, True, False, False, False)):
+    for k, skipped in enumerate((False, False, True, False, False, False, False)):
         skip.fill_(1 if skipped else 0)
-        Z.zero_adam_shard_step_dev_t(reps, n, gs, table, step, *dev, wd_mode="adamw", out=d_out, skip=skip)
-        # host t; past the 6-entry table the device takes entry 6, so the host passes t = 6 there
-        Z.zero_adam_shard_step(reps, n, 0.75, *host, Z.adam_hparams(step=min(t_host, 6), **kw),
-                               out=h_out, skip=skip)
+        Z.zero_adam_shard_step_dev_t(reps, n, gs, table, step, status, *dev, wd_mode="adamw", out=d_out,
+                                     skip=skip)
+        if t_host <= 6:                # the host steps only where the table has constants
+            Z.zero_adam_shard_step(reps, n, 0.75, *host, Z.adam_hparams(step=t_host, **kw),
+                                   out=h_out, skip=skip)
         torch.cuda.synchronize()
-        if not skipped:
+        refused = t_host > 6 and not skipped
+        if not skipped and not refused:
             t_host += 1
         assert int(step.item()) == t_host, k
+        assert int(status.item()) == (Z.ZERO_DEV_T_OUT_OF_TABLE if t_host > 6 and refused else 0), k
         for a, b, what in zip(dev, host, ("master", "m", "v")):
             assert_bits_equal(bits32(a), bits32(b), f"step {k} {what}")
         assert_bits_equal(bits16(d_out), bits16(h_out), f"step {k} params")
-    assert t_host == t0 + 5 and t_host - 1 > 6                          # the last steps used the clamp
+    assert t_host == 7 and int(status.item()) == Z.ZERO_DEV_T_OUT_OF_TABLE
+    status.zero_()
+    step.fill_(6)
     before = bits32(dev[0])
-    Z.zero_adam_shard_step_dev_t(reps, 0, gs, table, step, *dev)
+    Z.zero_adam_shard_step_dev_t(reps, 0, gs, table, step, status, *dev)
     torch.cuda.synchronize()
-    assert int(step.item()) == t_host + 1
+    assert int(step.item()) == 7 and int(status.item()) == 0
     assert_bits_equal(bits32(dev[0]), before, "n = 0")
+
+
+@pytest.mark.parametrize("t", [5, 4, 0, -3, 2 ** 40])
+def test_device_step_outside_table_refuses_update(t):
+    """A 3-entry constants table driven to a t it has no entry for (past it, at 0 or below, or
+    far past): master, m, v and the slot keep their bits, t stays, the status word is set. The
+    same call at t = 3 then updates as the host step does."""
+    n, R = 5 * TILE + 17, 8
+    rng = np.random.default_rng(41)
+    reps = [dev_rep(r, "bf16") for r in _reps_np(rng, R, n, "bf16")]
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    kw = dict(lr=1e-3, weight_decay=0.01, wd_mode="adamw")
+    table = Z.adam_table(Z.adam_hparams(**kw), 3, device=DEV)
+    dev = [dev_f32(master), dev_f32(np.full(n, 1e-4, np.float32)), dev_f32(np.full(n, 1e-8, np.float32))]
+    before = [bits32(x) for x in dev]
+    d_out = empty16(n, "bf16", fill=-5.0)
+    out_before = bits16(d_out)
+    step = torch.full((1,), t, dtype=torch.int64, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gs = torch.ones(1, device=DEV)
+    for _ in range(2):                 # twice: still refused, still no advance
+        Z.zero_adam_shard_step_dev_t(reps, n, gs, table, step, status, *dev, out=d_out)
+    torch.cuda.synchronize()
+    assert int(step.item()) == t and int(status.item()) == Z.ZERO_DEV_T_OUT_OF_TABLE
+    for a, b, what in zip(dev, before, ("master", "m", "v")):
+        assert_bits_equal(bits32(a), b, f"refused {what}")
+    assert_bits_equal(bits16(d_out), out_before, "refused slot")
+    # back inside the table: the update runs and matches the host step
+    step.fill_(3)
+    host = [x.clone() for x in dev]
+    h_out = empty16(n, "bf16")
+    Z.zero_adam_shard_step_dev_t(reps, n, gs, table, step, status, *dev, out=d_out)
+    Z.zero_adam_shard_step(reps, n, 1.0, *host, Z.adam_hparams(step=3, **kw), out=h_out)
+    torch.cuda.synchronize()
+    assert int(step.item()) == 4
+    for a, b, what in zip(dev, host, ("master", "m", "v")):
+        assert_bits_equal(bits32(a), bits32(b), f"t = 3 {what}")
+    assert_bits_equal(bits16(d_out), bits16(h_out), "t = 3 params")
 
 
 # --- IEEE special cases inside the update: subnormals, overflow, 0/0, inf/inf, signed zeros ----------

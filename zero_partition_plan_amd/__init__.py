@@ -19,7 +19,7 @@ __all__ = [
     "ZeroError", "ZeroPlan", "ZeroAdamHParams", "ZeroAdamScalars", "ZeroStageChoice",
     "ZeroOffloadBuffers", "lib", "lib_path", "offload_buffers",
     "ZERO_MAX_REPLICAS", "ZERO_MAX_SHARDS", "ZERO_F32", "ZERO_F16", "ZERO_BF16",
-    "ZERO_ADAMW", "ZERO_ADAM_L2", "adam_hparams",
+    "ZERO_ADAMW", "ZERO_ADAM_L2", "ZERO_DEV_T_OUT_OF_TABLE", "adam_hparams",
     "zero_partition_plan", "zero_shard_range", "zero_stage_bytes", "zero_stage_comm_bytes",
     "zero_choose_stage",
     "zero_adam_derive", "ZeroArenaArray", "zero_arena_layout", "zero_arena_alloc", "zero_arena_free",
@@ -37,6 +37,7 @@ ZERO_MAX_SHARDS = 64
 ZERO_OK, ZERO_E_INVAL, ZERO_E_OVERFLOW, ZERO_E_UNSUPPORTED, ZERO_E_HIP = range(5)
 ZERO_F32, ZERO_F16, ZERO_BF16 = 0, 1, 2
 ZERO_ADAMW, ZERO_ADAM_L2 = 0, 1
+ZERO_DEV_T_OUT_OF_TABLE = 1
 
 _TORCH_DT = {torch.float32: ZERO_F32, torch.float16: ZERO_F16, torch.bfloat16: ZERO_BF16}
 
@@ -130,8 +131,8 @@ def lib() -> ctypes.CDLL:
                                                P(ZeroAdamHParams), vp, i32, vp, vp],
             "zero_clip_scale": [vp, ctypes.c_double, ctypes.c_double, ctypes.c_double, vp, vp],
             "zero_adam_derive_table": [P(ZeroAdamHParams), u32, P(ZeroAdamScalars)],
-            "zero_adam_shard_step_dev_t": [P(_GradSrc), u64, vp, vp, u32, vp, i32, vp, vp, vp, vp,
-                                           i32, vp, vp],
+            "zero_adam_shard_step_dev_t": [P(_GradSrc), u64, vp, vp, u32, vp, vp, i32, vp, vp, vp,
+                                           vp, i32, vp, vp],
             "zero_gather_params": [P(vp), u32, u64, u32, u64, u64, vp, vp],
             "zero_host_adam_step": [vp, u64, ctypes.c_float, vp, vp, vp, P(ZeroAdamHParams), vp, i32,
                                     u32],
@@ -384,11 +385,13 @@ def zero_adam_shard_step_dev_scale(reps, n: int, grad_scale, master, m, v, hp: Z
         "zero_adam_shard_step_dev_scale")
 
 
-def zero_adam_shard_step_dev_t(reps, n: int, grad_scale, table, step, master, m, v,
+def zero_adam_shard_step_dev_t(reps, n: int, grad_scale, table, step, status, master, m, v,
                                wd_mode="adamw", out=None, skip=None, stream=None):
     """The step with its grad scale (float32 device tensor), constants table ((len, 9) float32
     device tensor, e.g. adam_table) and step counter (int64 device tensor) all on the device; the
-    counter advances on the device unless ``skip`` is set."""
+    counter advances on the device unless ``skip`` is set. A counter outside the table refuses the
+    update (nothing written, no advance) and sets ``status`` (int32 device tensor, zeroed by the
+    caller) to ZERO_DEV_T_OUT_OF_TABLE."""
     src, keep = _src(reps, n)
     f32 = (torch.float32,)
     out_dt = _out_dtype(out)
@@ -398,9 +401,10 @@ def zero_adam_shard_step_dev_t(reps, n: int, grad_scale, table, step, master, m,
     _check(lib().zero_adam_shard_step_dev_t(
         ctypes.byref(src), n, _ptr(grad_scale, 1, "grad_scale", f32),
         _ptr(table, table.numel(), "table", f32), table.shape[0],
-        _ptr(step, 1, "step", (torch.int64,)), int(mode), _ptr(master, n, "master", f32),
-        _ptr(m, n, "m", f32), _ptr(v, n, "v", f32), _ptr(out, n, "out"), out_dt,
-        _ptr(skip, 1, "skip", (torch.int32,)), _stream(stream)), "zero_adam_shard_step_dev_t")
+        _ptr(step, 1, "step", (torch.int64,)), _ptr(status, 1, "status", (torch.int32,)), int(mode),
+        _ptr(master, n, "master", f32), _ptr(m, n, "m", f32), _ptr(v, n, "v", f32),
+        _ptr(out, n, "out"), out_dt, _ptr(skip, 1, "skip", (torch.int32,)), _stream(stream)),
+        "zero_adam_shard_step_dev_t")
 
 
 def zero_clip_scale(sq, max_norm: float, clip_eps: float, inv_loss_scale: float, grad_scale,

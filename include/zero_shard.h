@@ -223,6 +223,26 @@ zero_status zero_reduce_shard(const zero_grad_src* src, uint64_t n, float* out_g
                               int32_t* d_nonfinite, double* d_sq_partials, double sq_scale,
                               void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): zero_reduce_shard with its squared-norm partials kept in a
+ * scratch array the library owns, followed by the squared-norm finish of zero_shard_sqnorm, so the
+ * caller passes only inputs and outputs. The result equals zero_reduce_shard(src, n, out_grad,
+ * d_nonfinite, partials, sq_scale) then zero_shard_sqnorm(NULL, n, sq_scale, partials, d_sq) bit
+ * for bit. out_grad (device float[n]) and d_nonfinite (device int32, OR-ed as there) are as in
+ * zero_reduce_shard; d_sq (device double, nullable) receives the squared norm. At least one output.
+ * The scratch is a static device array of ZERO_STATIC_SQ_PARTIALS doubles (32 MiB) on each GPU the
+ * library runs on, held until the process ends; it needs no clearing (every call overwrites what it
+ * reads). With d_sq, n may be at most ZERO_STATIC_MAX_ELEMS. It makes no allocation call: its
+ * first call on a device looks up that device's copy of the array. All calls on one GPU share the
+ * array, so calls that overlap in time on one GPU (other streams, other threads) race on it and
+ * must be ordered by the caller. Errors: as zero_reduce_shard; n > ZERO_STATIC_MAX_ELEMS with d_sq,
+ * d_sq overlapping a replica or out_grad -> ZERO_E_INVAL; the array's lookup failing -> ZERO_E_HIP. */
+#define ZERO_STATIC_SQ_PARTIALS (4u << 20)
+#define ZERO_STATIC_MAX_ELEMS (((uint64_t)ZERO_STATIC_SQ_PARTIALS - 1024u) * 256u)
+zero_status zero_reduce_shard_static(const zero_grad_src* src, uint64_t n, float* out_grad,
+                                     int32_t* d_nonfinite, double sq_scale, double* d_sq,
+                                     void* stream);
+
 /* Squared L2 norm of a shard in fp64, for gradient clipping. With d_grad != NULL, first writes the
  * per-tile partials of sum_i (double(d_grad[i]) * sq_scale)^2 into d_partials (as
  * zero_reduce_shard does); with d_grad == NULL, d_partials must already hold them from a

@@ -508,3 +508,27 @@ def test_arrays_off_natural_alignment_are_refused():
     assert L.zero_reduce_shard(ctypes.byref(good16), n, None, None, parts + 4, 1.0, None) == 1
     assert L.zero_shard_sqnorm(G + 1, n, 1.0, parts, parts - 8, None) == 1
     assert "not aligned" in Z.zero_last_error()
+
+
+def test_static_reduce_checks_its_reach_first():
+    """The no-allocation reduce refuses a shard its scratch cannot cover (only when a norm is
+    asked for), and checks aliasing and alignment, all before any device work."""
+    L = Z.lib()
+    fake = 1 << 40                                   # never dereferenced: every call below is invalid
+    src, keep = _src([fake], Z.ZERO_F16)
+    sq, G = fake + (64 << 30), fake + (128 << 30)
+    big = Z.ZERO_STATIC_MAX_ELEMS + 1
+    assert Z.ZERO_STATIC_MAX_ELEMS == 1_073_479_680
+    assert L.zero_reduce_shard_static(ctypes.byref(src), big, None, None, 1.0, sq, None) == 1
+    assert "exceeds" in Z.zero_last_error()
+    assert L.zero_reduce_shard_static(ctypes.byref(src), 100, None, None, 1.0, None, None) == 1
+    assert "no output" in Z.zero_last_error()
+    assert L.zero_reduce_shard_static(ctypes.byref(src), 100, None, None, 1.0, fake + 40, None) == 1
+    assert "d_sq overlaps replica 0" in Z.zero_last_error()
+    assert L.zero_reduce_shard_static(ctypes.byref(src), 100, G, None, 1.0, G + 8, None) == 1
+    assert L.zero_reduce_shard_static(ctypes.byref(src), 100, None, sq, 1.0, sq, None) == 1
+    assert "d_nonfinite overlaps d_sq" in Z.zero_last_error()
+    assert L.zero_reduce_shard_static(ctypes.byref(src), 100, None, None, 1.0, sq + 4, None) == 1
+    assert "not aligned" in Z.zero_last_error()
+    text = open(HEADER).read()
+    assert "#define ZERO_STATIC_SQ_PARTIALS (4u << 20)" in text

@@ -24,7 +24,8 @@ __all__ = [
     "zero_choose_stage",
     "zero_adam_derive", "ZeroArenaArray", "zero_arena_layout", "zero_arena_alloc", "zero_arena_free",
     "arena",
-    "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_adam_shard_step",
+    "zero_sq_partials_len", "zero_reduce_shard", "zero_shard_sqnorm", "zero_reduce_shard_static",
+    "ZERO_STATIC_SQ_PARTIALS", "ZERO_STATIC_MAX_ELEMS", "zero_adam_shard_step",
     "zero_adam_shard_step_dev_scale", "zero_clip_scale", "zero_adam_derive_table", "adam_table",
     "zero_adam_shard_step_dev_t",
     "AdamStep",
@@ -38,6 +39,8 @@ ZERO_OK, ZERO_E_INVAL, ZERO_E_OVERFLOW, ZERO_E_UNSUPPORTED, ZERO_E_HIP = range(5
 ZERO_F32, ZERO_F16, ZERO_BF16 = 0, 1, 2
 ZERO_ADAMW, ZERO_ADAM_L2 = 0, 1
 ZERO_DEV_T_OUT_OF_TABLE = 1
+ZERO_STATIC_SQ_PARTIALS = 4 << 20
+ZERO_STATIC_MAX_ELEMS = (ZERO_STATIC_SQ_PARTIALS - 1024) * 256
 
 _TORCH_DT = {torch.float32: ZERO_F32, torch.float16: ZERO_F16, torch.bfloat16: ZERO_BF16}
 
@@ -125,6 +128,7 @@ def lib() -> ctypes.CDLL:
             "zero_arena_free": [vp],
             "zero_reduce_shard": [P(_GradSrc), u64, vp, vp, vp, ctypes.c_double, vp],
             "zero_shard_sqnorm": [vp, u64, ctypes.c_double, vp, vp, vp],
+            "zero_reduce_shard_static": [P(_GradSrc), u64, vp, vp, ctypes.c_double, vp, vp],
             "zero_adam_shard_step": [P(_GradSrc), u64, ctypes.c_float, vp, vp, vp,
                                      P(ZeroAdamHParams), vp, i32, vp, vp],
             "zero_adam_shard_step_dev_scale": [P(_GradSrc), u64, vp, vp, vp, vp,
@@ -348,6 +352,17 @@ def zero_shard_sqnorm(grad, n: int, sq_scale: float, partials, out, stream=None)
         _ptr(grad, n, "grad", (torch.float32,)), n, float(sq_scale),
         _ptr(partials, zero_sq_partials_len(n), "partials", (torch.float64,)),
         _ptr(out, 1, "out", (torch.float64,)), _stream(stream)), "zero_shard_sqnorm")
+
+
+def zero_reduce_shard_static(reps, n: int, out_grad=None, nonfinite=None, sq=None,
+                             sq_scale: float = 1.0, stream=None):
+    """zero_reduce_shard then the squared-norm finish into ``sq`` (float64 device tensor), with the
+    partials in the library's own device scratch: no workspace argument, nothing allocated."""
+    src, keep = _src(reps, n)
+    _check(lib().zero_reduce_shard_static(
+        ctypes.byref(src), n, _ptr(out_grad, n, "out_grad", (torch.float32,)),
+        _ptr(nonfinite, 1, "nonfinite", (torch.int32,)), float(sq_scale),
+        _ptr(sq, 1, "sq", (torch.float64,)), _stream(stream)), "zero_reduce_shard_static")
 
 
 def _out_dtype(out) -> int:

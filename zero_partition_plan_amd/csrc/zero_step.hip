@@ -4,7 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "zero_internal.h"
 #include "zero_step.h"
@@ -21,6 +23,11 @@ using zero::step::StepScalars;
 
 constexpr int kWaves = kBlock / 64;
 constexpr uint32_t kSqLevel1 = 1024;   // second-level partial slots
+
+// The squared-norm partials of zero_reduce_shard_static, owned by the library: each GPU holds its
+// own copy from the code object's load until the process ends. In host code this name is a host
+// stand-in; device addresses come from hipGetSymbolAddress (static_scratch below).
+static __device__ __align__(256) double scratch[ZERO_STATIC_SQ_PARTIALS];
 
 // ---------------------------------------------------------------------------------------------
 // squared-norm finish, clip scale, step counter
@@ -89,6 +96,38 @@ __global__ __launch_bounds__(64) void k_step_advance(int64_t* __restrict__ step,
 
 // ---------------------------------------------------------------------------------------------
 // host side
+
+// ---------------------------------------------------------------------------------------------
+// the library's scratch, per device
+
+constexpr int kMaxDevices = 64;
+std::atomic<double*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// the device address of `scratch` on the current device, looked up once per device
+zero_status static_scratch(const char* fn, double** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return zero::fail(ZERO_E_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return zero::fail(ZERO_E_UNSUPPORTED, "%s: device index %d", fn, dev);
+  double* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || addr == nullptr)
+        return zero::fail(ZERO_E_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn,
+                          hipGetErrorString(e));
+      p = static_cast<double*>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ZERO_OK;
+}
 
 zero_status launched(const char* what) {
   const hipError_t e = hipGetLastError();
@@ -250,6 +289,53 @@ zero_status zero_shard_sqnorm(const float* d_grad, uint64_t n, double sq_scale, 
     }
   }
   return sq_finish(n, d_partials, d_out, st, fn);
+}
+
+zero_status zero_reduce_shard_static(const zero_grad_src* src, uint64_t n, float* out_grad,
+                                     int32_t* d_nonfinite, double sq_scale, double* d_sq,
+                                     void* stream) {
+  const char* fn = "zero_reduce_shard_static";
+  zero_status s = check_src(fn, src, n);
+  if (s != ZERO_OK) return s;
+  if (!out_grad && !d_nonfinite && !d_sq) return zero::fail(ZERO_E_INVAL, "%s: no output requested", fn);
+  if (d_sq && n > ZERO_STATIC_MAX_ELEMS)
+    return zero::fail(ZERO_E_INVAL, "%s: n = %llu exceeds the %llu elements the library's %u "
+                      "squared-norm partials cover", fn, (unsigned long long)n,
+                      (unsigned long long)ZERO_STATIC_MAX_ELEMS, (unsigned)ZERO_STATIC_SQ_PARTIALS);
+  const uint64_t rb = n * zero::dtype_bytes(src->dtype);
+  for (uint32_t k = 0; k < src->count; ++k) {
+    if (out_grad && zero::overlaps(out_grad, n * 4, src->ptrs[k], rb))
+      return zero::fail(ZERO_E_INVAL, "%s: out_grad overlaps replica %u", fn, k);
+    if (d_sq && zero::overlaps(d_sq, 8, src->ptrs[k], rb))
+      return zero::fail(ZERO_E_INVAL, "%s: d_sq overlaps replica %u", fn, k);
+  }
+  if (d_sq && out_grad && zero::overlaps(d_sq, 8, out_grad, n * 4))
+    return zero::fail(ZERO_E_INVAL, "%s: d_sq overlaps out_grad", fn);
+  if (d_nonfinite) {
+    const void* arr[2] = {out_grad, d_sq};
+    const uint64_t arr_b[2] = {out_grad ? n * 4 : 0, d_sq ? 8u : 0u};
+    const char* names[2] = {"out_grad", "d_sq"};
+    s = word_clear(fn, "d_nonfinite", d_nonfinite, 4, arr, arr_b, names, 2);
+    if (s == ZERO_OK) s = word_clear_reps(fn, "d_nonfinite", d_nonfinite, 4, src, rb);
+    if (s != ZERO_OK) return s;
+  }
+  s = src_natural(fn, src);
+  if (s != ZERO_OK) return s;
+  if ((out_grad && !aligned(out_grad, 4)) || (d_nonfinite && !aligned(d_nonfinite, 4)) ||
+      (d_sq && !aligned(d_sq, 8)))
+    return zero::fail(ZERO_E_INVAL, "%s: out_grad, d_nonfinite or d_sq is not aligned to its "
+                      "elements", fn);
+  double* partials = nullptr;
+  if (d_sq) {
+    s = static_scratch(fn, &partials);
+    if (s != ZERO_OK) return s;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n > 0) {
+    s = reduce_impl(src, n, out_grad, d_nonfinite, partials, sq_scale, st, fn);
+    if (s != ZERO_OK) return s;
+  }
+  return d_sq ? sq_finish(n, partials, d_sq, st, fn) : zero::ok();
 }
 
 }  // extern "C"

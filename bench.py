@@ -154,15 +154,19 @@ def shard_elems(w) -> int:
     return per
 
 
-def launch_elems(workload: str) -> int:
-    """Shard elements one launch of the dominant kernel covers (the mean, for the layer gather)."""
+def launch_elems(workload: str) -> float:
+    """Shard elements one launch of the dominant kernel covers, as the mean over one step's launches
+    (the layer gather's layers differ in size, and a windowed shard ends in a shorter window), so
+    that bytes per element x this / the mean launch time is the step's algorithmic bytes over its
+    total kernel time."""
     from workloads import WORKLOADS
     if workload == "gather7b":
-        return WORKLOADS["llama7b"].n // GATHER_LAYERS
+        return WORKLOADS["llama7b"].n / GATHER_LAYERS
     if workload == "offload7b":
         return OFFLOAD_CHUNK
     w = WORKLOADS["llama13b" if workload.startswith("llama13b") else workload]
-    return min(shard_elems(w), w.window or shard_elems(w))
+    S = shard_elems(w)
+    return S / -(-S // (w.window or S))
 
 
 def launches_per_step(workload: str) -> int:
@@ -260,7 +264,8 @@ def summarize(workload: str):
              f"- command (repo root): `{cmds['trace']}`",
              f"- GPU: {_agent(dirs['trace'])}",
              f"- kernel source sha256[:16]: `{src_hash}`",
-             f"- workload: {WL_DESC[workload]}; {n_launch:,} shard elements per launch", "",
+             f"- workload: {WL_DESC[workload]}; {n_launch:,.0f} shard elements per launch (mean over "
+             f"a step's launches)", "",
              "| kernel | calls | avg ms | min ms | max ms | share | algorithmic GB/s at avg |",
              "|---|---|---|---|---|---|---|"]
     for r in stats:
@@ -406,6 +411,108 @@ def placement_context(name: str, steps: int = 5):
     return {"separate_ms_per_step": ms, "steps": steps,
             "note": "the same step with master, m, v, every replica row and the output each in its own "
                     "allocation; the timed line above places them in one arena (zero_arena_layout)"}
+
+
+def _interleaved(legs, calls: int = 5, rounds: int = 3):
+    """ms per call of each (name, fn) leg, timed in alternation (calls per leg per round, rounds
+    rounds) so that drift on the box hits every leg alike; the median round of each."""
+    import torch
+    got = {name: [] for name, _ in legs}
+    for _ in range(rounds):
+        for name, fn in legs:
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = new_event(True), new_event()
+            for _ in range(calls):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            got[name].append(e0.elapsed_time(e1) / calls)
+    return {name: pct(xs, 0.5) for name, xs in got.items()}
+
+
+def odd_slot_context(st):
+    """The 7B step with its slot one element past its place (2 bytes past a 4-byte word, as rank
+    r's slot r*S of the gathered buffer is when S is odd: the word-realigning store path), against
+    the aligned step, timed in alternation in the same arena."""
+    import zero_partition_plan_amd as Z
+    inp, S, b = st["inp"], st["S"], st["begin"]
+    odd = Z.AdamStep(inp["reps"], S, inp["master"], inp["m"], inp["v"], out=st["full"][b + 1:b + 1 + S])
+
+    def aligned():
+        step_fused(st, Spans(False))
+
+    def shifted():
+        odd(1.0, hparams(st))
+        st["t"] += 1
+
+    ms = _interleaved([("aligned", aligned), ("odd_slot", shifted)])
+    byts = kernel_bytes_per_elem("llama7b")["k_adam_step"] * S
+    return {"aligned_ms": ms["aligned"], "odd_slot_ms": ms["odd_slot"],
+            "odd_slot_gbs": byts / ms["odd_slot"] / 1e6,
+            "odd_over_aligned_rate": ms["aligned"] / ms["odd_slot"],
+            "note": "the same step with the 16-bit slot starting 2 bytes past a 4-byte word (rank r's "
+                    "slot when S is odd), median of 3 alternating rounds of 5 steps"}
+
+
+_CEILING = None
+
+
+def ceiling_lib():
+    """The benchmark's measurement kernels (libzero_ceiling.so: traffic twin, triad)."""
+    global _CEILING
+    if _CEILING is None:
+        import ctypes
+        path = os.path.join(ROOT, "zero_partition_plan_amd", "libzero_ceiling.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run `python -m zero_partition_plan_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, u64, u32, f32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_float
+        L.zero_ceiling_twin.argtypes = [ctypes.POINTER(vp), u32, u64, vp, vp, vp, vp, f32, vp]
+        L.zero_ceiling_triad.argtypes = [vp, vp, u64, f32, vp]
+        L.zero_ceiling_twin.restype = L.zero_ceiling_triad.restype = ctypes.c_int
+        _CEILING = L
+    return _CEILING
+
+
+def ceiling_context(st):
+    """What this machine's memory system gives the step's own access pattern, in the same process and
+    on the step's own arrays in its arena: the fused step's traffic twin (the same 11 read and 4
+    write streams and bytes, trivial arithmetic) and a 2:1 in-place triad over master and m (two
+    fp32 reads, one write), timed in alternation with the step. Both leave the data unchanged."""
+    import ctypes
+
+    import torch
+    L = ceiling_lib()
+    inp, S = st["inp"], st["S"]
+    reps = inp["reps"]
+    rows = list(reps.unbind(0)) if isinstance(reps, torch.Tensor) else list(reps)
+    ptrs = (ctypes.c_void_p * len(rows))(*[r.data_ptr() for r in rows])
+    P, M, V = (inp[k].data_ptr() for k in ("master", "m", "v"))
+    out = st["slot"].data_ptr()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def twin():
+        if L.zero_ceiling_twin(ptrs, len(rows), S, P, M, V, out, 0.0, stream) != 0:
+            raise RuntimeError("zero_ceiling_twin refused its arguments")
+
+    def triad():
+        if L.zero_ceiling_triad(P, M, S, 0.0, stream) != 0:
+            raise RuntimeError("zero_ceiling_triad refused its arguments")
+
+    def step():
+        step_fused(st, Spans(False))
+
+    ms = _interleaved([("step", step), ("twin", twin), ("triad", triad)])
+    bpe = kernel_bytes_per_elem("llama7b")["k_adam_step"]
+    step_gbs, twin_gbs, triad_gbs = bpe * S / ms["step"] / 1e6, bpe * S / ms["twin"] / 1e6, 12 * S / ms["triad"] / 1e6
+    return {"step_gbs": step_gbs, "twin_gbs": twin_gbs, "twin_frac": twin_gbs / HBM_PEAK_GBS,
+            "triad_gbs": triad_gbs, "triad_frac": triad_gbs / HBM_PEAK_GBS,
+            "step_over_twin": step_gbs / twin_gbs,
+            "note": "same process, same arena: the step's traffic twin moves the step's 42 B per "
+                    "element with trivial math (this box's ceiling for that mix); the triad moves "
+                    "12 B per element (2 fp32 reads : 1 write); medians of 3 alternating rounds of 5 "
+                    "calls"}
 
 
 def setup_gather():
@@ -984,7 +1091,15 @@ def main(argv=None):
         nvtx.range_push("context legs")
         context = {"copy_ceiling": copy_ceiling()}
         log(f"copy ceiling: {context['copy_ceiling']['gbs']:.0f} GB/s")
+        context["odd_slot"] = odd_slot_context(st)
+        log(f"odd slot: {context['odd_slot']['odd_slot_ms']:.4f} ms per step against "
+            f"{context['odd_slot']['aligned_ms']:.4f} aligned")
         if args.placement == "arena":
+            context["ceiling"] = ceiling_context(st)
+            c = context["ceiling"]
+            log(f"same-arena ceilings: step {c['step_gbs']:.0f} GB/s, traffic twin {c['twin_gbs']:.0f} "
+                f"GB/s ({100 * c['twin_frac']:.1f}% of peak), triad {c['triad_gbs']:.0f} GB/s; "
+                f"step / twin {c['step_over_twin']:.3f}")
             context["placement"] = placement_context(args.workload)
             log(f"separate allocations: {context['placement']['separate_ms_per_step']:.4f} ms per step")
         nvtx.range_pop()

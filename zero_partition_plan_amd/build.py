@@ -19,6 +19,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libzero_shard.so")
+# the benchmark's measurement kernels (traffic twin, triad): a library of their own, not the step's
+CEILING_LIB = os.path.join(PKG, "libzero_ceiling.so")
+CEILING_SOURCES = [os.path.join(CSRC, "zero_ceiling.hip")]
 SOURCES = [os.path.join(CSRC, "zero_host.cpp"), os.path.join(CSRC, "zero_step.hip"),
            os.path.join(CSRC, "zero_gather.hip"), os.path.join(CSRC, "zero_host_adam.cpp"),
            os.path.join(CSRC, "zero_offload.cpp"), os.path.join(CSRC, "zero_arena.cpp")]
@@ -64,26 +67,33 @@ def _run(cmd, verbose):
 
 
 def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = False,
-          jobs: int | None = None) -> str:
-    """Compile the library to ``out`` (atomically replaced) and return its path. The objects build
-    in parallel (``jobs`` processes, default: the CPU count, at most 16) in a scratch directory."""
+          jobs: int | None = None, ceiling_out: str | None = CEILING_LIB) -> str:
+    """Compile the library to ``out`` (atomically replaced) and return its path; with
+    ``ceiling_out``, also the measurement library there. The objects build in parallel (``jobs``
+    processes, default: the CPU count, at most 16) in a scratch directory."""
     import concurrent.futures
     import tempfile
     base = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     base += [f"-D{d}" for d in (defines or [])]
     jobs = jobs or min(16, os.cpu_count() or 1)
     with tempfile.TemporaryDirectory(prefix="zero_build_") as tmpdir:
-        cmds, objs = [], []
-        for src, defs, stem in _units():
+        cmds, objs, ceil_objs = [], [], []
+        units = [(u, objs) for u in _units()]
+        if ceiling_out:
+            units += [((src, [], "ceil_" + os.path.splitext(os.path.basename(src))[0]), ceil_objs)
+                      for src in CEILING_SOURCES]
+        for (src, defs, stem), dest in units:
             obj = os.path.join(tmpdir, stem + ".o")
             cmds.append([*base, "-c", *[f"-D{d}" for d in defs], "-o", obj, src])
-            objs.append(obj)
+            dest.append(obj)
         with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()
-        tmp = out + ".tmp"
-        _run([hipcc(), *FLAGS, "-shared", "-o", tmp, *objs], verbose)
-    os.replace(tmp, out)
+        links = [(out, objs)] + ([(ceiling_out, ceil_objs)] if ceiling_out else [])
+        for dst, os_ in links:
+            _run([hipcc(), *FLAGS, "-shared", "-o", dst + ".tmp", *os_], verbose)
+        for dst, _ in links:
+            os.replace(dst + ".tmp", dst)
     return out
 
 
@@ -91,8 +101,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("-D", dest="defines", action="append", default=[])
     ap.add_argument("--out", default=LIB)
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the measurement library")
     args = ap.parse_args(argv)
-    print(build(args.out, args.defines, verbose=True))
+    print(build(args.out, args.defines, verbose=True, ceiling_out=None if args.no_ceiling else CEILING_LIB))
 
 
 if __name__ == "__main__":

@@ -250,23 +250,33 @@ __device__ __forceinline__ float sum_reps1(const RepPtrs& reps, int nrep, uint64
   return a;
 }
 
-// 16-bit output of elements [i, i+4). With MIS and an output starting at an odd element, the
-// words are (i-1, i), (i+1, i+2) and (i+3, i+4): each lane writes its middle word and the word it
-// shares with the lane before it (that lane's last element comes over by a shuffle); the first
-// lane of a wave writes its first element and the last lane its last element as 16-bit stores,
-// so no byte outside [i, i+4) of the wave's run is written.
-template <int ODT, bool MIS>
+// 16-bit output of elements [i, i+4). MIS (see k_adam_step) 1: the output starts at an odd
+// element; 2: it may (out_odd says). Then the words are (i-1, i), (i+1, i+2) and (i+3, i+4): each
+// lane but the first writes the 8 bytes (i-1, i, i+1, i+2) in one store, the element i-1 coming
+// over from the lane before it by a shuffle, so a wave's stores cover one contiguous run and only
+// the lines at its two ends are shared with the neighbouring waves. The first lane writes i as a
+// 16-bit store and (i+1, i+2) as a word, and the last lane also writes i+3 as a 16-bit store, so
+// no byte outside the wave's 256 elements is written.
+template <int ODT, int MIS>
 __device__ __forceinline__ void store_out4(void* out, uint64_t i, const f32x4& p, uint32_t out_odd) {
   const uint32_t lo = pack2<ODT>(p.x, p.y), hi = pack2<ODT>(p.z, p.w);
   uint16_t* o = static_cast<uint16_t*>(out) + i;
-  if constexpr (MIS) {
-    if (out_odd) {
+  if constexpr (MIS != 0) {
+    if (MIS == 1 || out_odd) {
       const uint32_t left = (uint32_t)__shfl_up((int)hi, 1, 64);   // the previous lane's (i-2, i-1)
+      const uint32_t mid = __builtin_amdgcn_alignbyte(hi, lo, 2);   // (i+1, i+2)
       const int lane = threadIdx.x & 63;
-      st(reinterpret_cast<uint32_t*>(o + 1), __builtin_amdgcn_alignbyte(hi, lo, 2));
-      if (lane != 0) st(reinterpret_cast<uint32_t*>(o - 1), __builtin_amdgcn_alignbyte(lo, left, 2));
-      else st(o, (uint16_t)(lo & 0xffffu));
-      if (lane == 63) st(o + 3, (uint16_t)(hi >> 16));
+      // plain (write-back) stores here, not non-temporal ones: the pieces of a line shared with
+      // the neighbouring waves then meet in L2 and go to memory as one line. Measured on MI355X
+      // for the 7B step: 6.33 ms with non-temporal stores, 5.84 with plain stores at the ends only,
+      // 5.61 with plain stores throughout, against 5.55 ms for an aligned slot.
+      if (lane != 0) {
+        *reinterpret_cast<u32x2w*>(o - 1) = u32x2{__builtin_amdgcn_alignbyte(lo, left, 2), mid};
+      } else {
+        *o = (uint16_t)(lo & 0xffffu);
+        *reinterpret_cast<uint32_t*>(o + 1) = mid;
+      }
+      if (lane == 63) *(o + 3) = (uint16_t)(hi >> 16);
       return;
     }
   }
@@ -309,7 +319,10 @@ __device__ __forceinline__ void adam_elem(const RepPtrs& reps, int nrep, uint64_
   if constexpr (ODT != ZERO_F32) static_cast<uint16_t*>(out)[i] = to_out1<ODT>(p);
 }
 
-template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL, bool DGS, bool MIS>
+// MIS 0: every 16-bit array starts on a 4-byte word; 1: the output starts at an odd element and
+// the replicas on words; 2: replicas may start at odd elements (Phase.rep_odd) and so may the
+// output (Phase.out_odd)
+template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL, bool DGS, int MIS>
 __global__ __launch_bounds__(kAdamBlock) void k_adam_step(
     RepPtrs reps, int nrep, uint64_t first_tile, StepScalars sc, float* __restrict__ P,
     float* __restrict__ M, float* __restrict__ V, void* __restrict__ out,
@@ -345,7 +358,7 @@ __global__ __launch_bounds__(kAdamBlock) void k_adam_step(
     m[u] = ldw4(M + idx[u]);
     v[u] = ldw4(V + idx[u]);
   }
-  sum_reps4<RDT, RFIX, SUB, MIS>(reps, nrep, ph.rep_odd, idx, acc);
+  sum_reps4<RDT, RFIX, SUB, MIS == 2>(reps, nrep, ph.rep_odd, idx, acc);
   unroll<SUB>([&](auto u) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -445,7 +458,7 @@ __global__ __launch_bounds__(64) void k_reduce(RepPtrs reps, int nrep, uint64_t 
 // ---------------------------------------------------------------------------------------------
 // Adam dispatch
 
-template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL, bool MIS>
+template <int RDT, int ODT, bool L2, int RFIX, bool SKIP, bool TAIL, int MIS>
 void launch_adam_grid(const AdamArgs& a, uint64_t t0, uint64_t blocks) {
   if (a.dc.gs != nullptr)
     hipLaunchKernelGGL((k_adam_step<RDT, ODT, L2, RFIX, SKIP, TAIL, true, MIS>),
@@ -457,7 +470,7 @@ void launch_adam_grid(const AdamArgs& a, uint64_t t0, uint64_t blocks) {
                        a.sc, a.P, a.M, a.V, a.out, a.skip, a.dc, a.n, a.ph);
 }
 
-template <int RDT, int ODT, bool L2, int RFIX, bool MIS>
+template <int RDT, int ODT, bool L2, int RFIX, int MIS>
 void launch_adam_tiles(const AdamArgs& a) {
   // Grids of at most kMaxGrid tiles, each told where its first tile is. A partial last tile
   // rides on the last grid as one extra block (TAIL); a shard shorter than one tile is then a
@@ -478,7 +491,7 @@ void launch_adam_tiles(const AdamArgs& a) {
   } while (t0 < a.ntiles);
 }
 
-template <int RDT, int ODT, bool L2, bool MIS>
+template <int RDT, int ODT, bool L2, int MIS>
 void launch_adam_by_count(const AdamArgs& a) {
   switch (a.nrep) {
     case 1: launch_adam_tiles<RDT, ODT, L2, 1, MIS>(a); break;
@@ -491,12 +504,14 @@ void launch_adam_by_count(const AdamArgs& a) {
 
 template <int RDT, int ODT, bool L2>
 void launch_adam_l2(const AdamArgs& a) {
-  // fp32 replicas with no 16-bit output have nothing that can start at an odd element
-  constexpr bool kCanMis = !(RDT == ZERO_F32 && ODT == ZERO_F32);
-  if (kCanMis && (a.ph.rep_odd != 0 || a.ph.out_odd != 0))
-    launch_adam_by_count<RDT, ODT, L2, kCanMis>(a);
-  else
-    launch_adam_by_count<RDT, ODT, L2, false>(a);
+  // only 16-bit replicas and a 16-bit output can start at an odd element
+  if constexpr (RDT != ZERO_F32) {
+    if (a.ph.rep_odd != 0) return launch_adam_by_count<RDT, ODT, L2, 2>(a);
+  }
+  if constexpr (ODT != ZERO_F32) {
+    if (a.ph.out_odd != 0) return launch_adam_by_count<RDT, ODT, L2, 1>(a);
+  }
+  launch_adam_by_count<RDT, ODT, L2, 0>(a);
 }
 
 // ---------------------------------------------------------------------------------------------

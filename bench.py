@@ -78,6 +78,9 @@ WL_DESC = {
 GATHER_LAYERS = 34          # embeddings, 32 blocks, final norm + head
 OFFLOAD_CHUNK = 32 << 20    # elements per pipeline chunk
 OFFLOAD_THREADS = 16        # host threads: a 16-core host share per GPU
+# default timed steps per workload: about 5 s of timed work each
+DEFAULT_STEPS = {"llama7b": 1000, "gpt2": 10000, "llama13b": 500, "llama13b-clean": 500, "gpt3": 60,
+                 "gather7b": 300, "offload7b": 30}
 
 
 def log(msg):
@@ -936,7 +939,10 @@ def cpu_baseline(name: str, seconds: float):
 def main(argv=None):
     ap = argparse.ArgumentParser(description="sharded ZeRO AdamW step benchmark")
     ap.add_argument("--gpus", type=int, default=1, help="GPUs (only 1: one rank's shard on one GPU)")
-    ap.add_argument("--steps", type=int, default=20, help="timed steps")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: about 5 s of timed work for the workload, so that a "
+                         "GPU-utilisation sampler sees the run: " +
+                         ", ".join(f"{k} {v}" for k, v in DEFAULT_STEPS.items()) + ")")
     ap.add_argument("--warmup", type=int, default=3, help="untimed steps first")
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "gpt2", "llama13b", "llama13b-clean", "gpt3", "gather7b",
@@ -962,6 +968,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.config is not None:
         args.workload = {2: "gpt2", 3: "llama7b", 4: "llama13b", 5: "gpt3"}[args.config]
+    if args.steps is None:
+        args.steps = DEFAULT_STEPS[args.workload]
     if args.profile_commands:
         for k, c in profile_commands(args.workload).items():
             print(f"{c} > {profile_dirs(args.workload)[k]}.log 2>&1")

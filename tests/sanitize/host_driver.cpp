@@ -9,6 +9,7 @@
 
 #include <vector>
 
+#include "zero_host_adam.h"
 #include "zero_shard.h"
 
 static int failures = 0;
@@ -154,6 +155,39 @@ static void host_updates() {
          ZERO_E_OVERFLOW);
 }
 
+// the offloaded step's thread team: consecutive jobs of different sizes on one team (as the step's
+// chunks run) give the same bits as the per-call threads, for every team size
+static void teams() {
+  const uint64_t sizes[] = {0, 1, 70001, 300007, 5, 131072, 65536 * 3 + 1};
+  uint64_t seed = 9;
+  const uint64_t nmax = 300007;
+  std::vector<float> g(nmax), p0(nmax), m0(nmax), v0(nmax);
+  for (uint64_t i = 0; i < nmax; ++i) {
+    g[i] = ((int)(lcg(&seed) % 2001) - 1000) * 1e-6f;
+    p0[i] = ((int)(lcg(&seed) % 2001) - 1000) * 2e-5f;
+    m0[i] = ((int)(lcg(&seed) % 2001) - 1000) * 1e-7f;
+    v0[i] = (lcg(&seed) % 1000) * 1e-10f;
+  }
+  zero_adam_hparams hp = {1e-3, 0.9, 0.999, 1e-8, 0.01, ZERO_ADAMW, 0, 5};
+  zero_adam_scalars k;
+  EXPECT(zero_adam_derive(&hp, &k) == ZERO_OK);
+  for (uint32_t t : {1u, 2u, 3u, 16u}) {
+    zero::HostTeam team(t);
+    EXPECT(team.size() >= 1 && team.size() <= t);
+    for (int rep = 0; rep < 2; ++rep)
+      for (uint64_t n : sizes) {
+        std::vector<float> pa = p0, ma = m0, va = v0, pb = p0, mb = m0, vb = v0;
+        std::vector<uint16_t> oa(nmax, 0x1111), ob(nmax, 0x1111);
+        EXPECT(zero::host_step(g.data(), n, 0.5f, pa.data(), ma.data(), va.data(), k, false, oa.data(),
+                               ZERO_BF16, t, &team) == ZERO_OK);
+        EXPECT(zero::host_step(g.data(), n, 0.5f, pb.data(), mb.data(), vb.data(), k, false, ob.data(),
+                               ZERO_BF16, t) == ZERO_OK);
+        EXPECT(memcmp(pa.data(), pb.data(), nmax * 4) == 0 && memcmp(va.data(), vb.data(), nmax * 4) == 0);
+        EXPECT(memcmp(oa.data(), ob.data(), nmax * 2) == 0);
+      }
+  }
+}
+
 static void arenas() {
   uint64_t seed = 7;
   for (int trial = 0; trial < 200; ++trial) {
@@ -193,6 +227,7 @@ int main() {
   arenas();
   derive();
   host_updates();
+  teams();
   if (failures) {
     fprintf(stderr, "%d expectation(s) failed\n", failures);
     return 1;

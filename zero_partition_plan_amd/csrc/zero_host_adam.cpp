@@ -44,6 +44,9 @@ inline uint16_t f16_rne(float x) {
   return (uint16_t)(sign | h);
 }
 
+}  // namespace
+
+namespace zero {
 struct HostStep {
   const float* g;
   float gs;
@@ -51,6 +54,11 @@ struct HostStep {
   uint16_t* out;
   zero_adam_scalars k;
 };
+}  // namespace zero
+
+namespace {
+
+using zero::HostStep;
 
 template <bool L2, int ODT>
 inline __attribute__((always_inline)) void adam_range(const HostStep& s, uint64_t lo, uint64_t hi) {
@@ -82,7 +90,7 @@ __attribute__((target("avx2"))) void range_avx2(const HostStep& s, uint64_t lo, 
   adam_range<L2, ODT>(s, lo, hi);
 }
 
-typedef void (*RangeFn)(const HostStep&, uint64_t, uint64_t);
+typedef zero::HostRangeFn RangeFn;
 
 template <bool L2>
 RangeFn pick_odt(int odt, bool avx2) {
@@ -91,16 +99,27 @@ RangeFn pick_odt(int odt, bool avx2) {
   return avx2 ? range_avx2<L2, ZERO_F32> : range_base<L2, ZERO_F32>;
 }
 
-void run_threads(RangeFn fn, const HostStep& s, uint64_t n, uint32_t threads) {
+uint32_t hw_threads(uint32_t threads) {
   if (threads == 0) threads = std::thread::hardware_concurrency();
-  if (threads == 0) threads = 1;
+  return threads == 0 ? 1 : threads;
+}
+
+// threads actually used for n elements, and the length of each one's range
+void split(uint64_t n, uint32_t& threads, uint64_t& per) {
   const uint64_t kGrain = 1u << 16;  // keep thread ranges at least this long
   if ((uint64_t)threads > (n + kGrain - 1) / kGrain) threads = (uint32_t)((n + kGrain - 1) / kGrain);
+  if (threads < 1) threads = 1;
+  per = ((n + threads - 1) / threads + 63) / 64 * 64;  // 256-byte aligned splits
+}
+
+void run_threads(RangeFn fn, const HostStep& s, uint64_t n, uint32_t threads) {
+  threads = hw_threads(threads);
+  uint64_t per = 0;
+  split(n, threads, per);
   if (threads <= 1) {
     fn(s, 0, n);
     return;
   }
-  const uint64_t per = ((n + threads - 1) / threads + 63) / 64 * 64;  // 256-byte aligned splits
   // No exception may leave a C entry point: a range whose thread cannot be started (or whose
   // bookkeeping cannot be allocated) runs on the calling thread instead.
   std::vector<std::thread> pool;
@@ -132,13 +151,85 @@ bool have_avx2() {
 
 namespace zero {
 
+HostTeam::HostTeam(uint32_t threads) {
+  threads = hw_threads(threads);
+  try {
+    workers_.reserve(threads - 1);
+    for (uint32_t t = 1; t < threads; ++t) workers_.emplace_back(&HostTeam::work, this, t);
+  } catch (...) {
+    // fewer members: the ones that started serve; run() splits over size()
+  }
+}
+
+HostTeam::~HostTeam() {
+  {
+    std::lock_guard<std::mutex> lock(mu_);
+    stop_ = true;
+  }
+  go_.notify_all();
+  for (auto& th : workers_) th.join();
+}
+
+void HostTeam::work(uint32_t member) {
+  uint64_t seen = 0;
+  for (;;) {
+    HostRangeFn fn;
+    const HostStep* s;
+    uint64_t lo = 0, hi = 0;
+    bool mine = false;
+    {
+      std::unique_lock<std::mutex> lock(mu_);
+      go_.wait(lock, [&] { return stop_ || generation_ != seen; });
+      if (stop_) return;
+      seen = generation_;
+      fn = fn_;
+      s = step_;
+      if (member < used_) {
+        lo = per_ * member;
+        hi = lo + per_ < n_ ? lo + per_ : n_;
+        mine = lo < hi;
+      }
+    }
+    if (mine) fn(*s, lo, hi);
+    {
+      std::lock_guard<std::mutex> lock(mu_);
+      if (--pending_ == 0) done_.notify_one();
+    }
+  }
+}
+
+void HostTeam::run(HostRangeFn fn, const HostStep& s, uint64_t n) {
+  uint32_t threads = size();
+  uint64_t per = 0;
+  split(n, threads, per);
+  if (threads <= 1 || workers_.empty()) {
+    fn(s, 0, n);
+    return;
+  }
+  {
+    std::lock_guard<std::mutex> lock(mu_);
+    fn_ = fn;
+    step_ = &s;
+    n_ = n;
+    per_ = per;
+    used_ = threads;
+    pending_ = (uint32_t)workers_.size();
+    ++generation_;
+  }
+  go_.notify_all();
+  fn(s, 0, per < n ? per : n);
+  std::unique_lock<std::mutex> lock(mu_);
+  done_.wait(lock, [&] { return pending_ == 0; });
+}
+
 zero_status host_step(const float* grad, uint64_t n, float grad_scale, float* master, float* m,
                       float* v, const zero_adam_scalars& k, bool l2, void* out, int out_dtype,
-                      uint32_t threads) {
+                      uint32_t threads, HostTeam* team) {
   HostStep s{grad, grad_scale, master, m, v, static_cast<uint16_t*>(out), k};
   const int odt = out ? out_dtype : ZERO_F32;
   const RangeFn fn = l2 ? pick_odt<true>(odt, have_avx2()) : pick_odt<false>(odt, have_avx2());
-  run_threads(fn, s, n, threads);
+  if (team != nullptr) team->run(fn, s, n);
+  else run_threads(fn, s, n, threads);
   return ZERO_OK;
 }
 

@@ -5,7 +5,8 @@
 // zero_offload_step runs the whole offloaded step for a rank's shard in chunks, double-buffered:
 // the GPU sums the gradient replicas of chunk c+1 and copies it to pinned host memory while the
 // host updates chunk c (zero_host_adam.cpp), and chunk c's 16-bit parameters are copied back to
-// the rank's slot on a second stream while the host works on chunk c+1.
+// the rank's slot on a second stream while the host works on chunk c+1. The host threads are
+// started once per call and serve every chunk.
 #include <hip/hip_runtime_api.h>
 
 #include "zero_host_adam.h"
@@ -53,6 +54,8 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
   }
   const bool l2 = hp->wd_mode == ZERO_ADAM_L2;
   const uint64_t nchunks = (n + C - 1) / C;
+  // one team of host threads for every chunk of this call (threads that cannot start are left out)
+  zero::HostTeam team(buf->threads);
   const void* ptrs[ZERO_MAX_REPLICAS];   // one chunk's replica pointers (no allocation)
   bool sent_any[2] = {false, false};
 
@@ -85,7 +88,7 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
     if (e != hipSuccess) break;
     uint16_t* hp16 = static_cast<uint16_t*>(buf->h_param) + b * C;
     zero::host_step(buf->h_grad + b * C, len, grad_scale, h_master + off, h_m + off, h_v + off, k, l2,
-              hp16, out_dtype, buf->threads);
+                    hp16, out_dtype, buf->threads, &team);
     e = hipMemcpyAsync(static_cast<uint16_t*>(d_out_param) + off, hp16, len * 2,
                        hipMemcpyHostToDevice, back);
     if (e == hipSuccess) e = hipEventRecord(sent[b], back);

@@ -367,6 +367,8 @@ typedef struct {
   uint32_t threads;     /* host threads for the update (0 = all) */
   uint32_t reserved;
   void* h2d_stream;     /* stream for the parameter copies back to the GPU (NULL = `stream`) */
+  void* events[4];      /* four distinct hipEvent_t made by the caller (timing may be disabled); the
+                           call records and waits on them (two per staging buffer) and leaves them */
 } zero_offload_buffers;
 
 /* One rank's offloaded step (P2 ZeRO-Offload): for each chunk of the shard, the GPU sums the
@@ -376,10 +378,11 @@ typedef struct {
  * fp16). Chunks are double-buffered: the GPU reduces and copies chunk c+1 while the host updates
  * chunk c, and chunk c's parameters travel back on h2d_stream while the host works on the next.
  * Results equal zero_adam_shard_step's bit for bit. Host-synchronous: returns once every parameter
- * copy has landed; it creates and destroys four HIP events per call. Aliasing: d_out_param, the
- * staging d_grad and the replicas must not overlap. Errors: as zero_host_adam_step and
- * zero_reduce_shard, plus NULL or incomplete buffers or device aliasing -> ZERO_E_INVAL and HIP
- * failures -> ZERO_E_HIP (the state may then be partly updated). */
+ * copy has landed. It allocates nothing and creates no HIP objects (the staging and the events are
+ * the caller's); its host threads are started once per call and serve every chunk. Aliasing:
+ * d_out_param, the staging d_grad and the replicas must not overlap. Errors: as zero_host_adam_step
+ * and zero_reduce_shard, plus NULL or incomplete buffers (a NULL or repeated event) or device
+ * aliasing -> ZERO_E_INVAL and HIP failures -> ZERO_E_HIP (the state may then be partly updated). */
 zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_scale,
                               float* h_master, float* h_m, float* h_v, const zero_adam_hparams* hp,
                               void* d_out_param, int32_t out_dtype,

@@ -532,3 +532,27 @@ def test_static_reduce_checks_its_reach_first():
     assert "not aligned" in Z.zero_last_error()
     text = open(HEADER).read()
     assert "#define ZERO_STATIC_SQ_PARTIALS (4u << 20)" in text
+
+
+def test_offload_step_needs_four_distinct_events():
+    """zero_offload_step creates no HIP objects: its four events come with the caller's staging,
+    and a NULL or repeated one is refused before any device work."""
+    L = Z.lib()
+    fake = 1 << 40                                   # never dereferenced: every call below is invalid
+    hp = Z.adam_hparams()
+    src, keep = _src([fake], Z.ZERO_BF16)
+    h = (ctypes.c_float * 64)()
+    hm, hv = (ctypes.c_float * 64)(), (ctypes.c_float * 64)()
+    ev = [fake + 0x100, fake + 0x200, fake + 0x300, fake + 0x400]
+
+    def bufs(events):
+        return Z.ZeroOffloadBuffers(fake + (1 << 20), fake + (2 << 20), fake + (3 << 20), 16, 1, 0, None,
+                                    (ctypes.c_void_p * 4)(*events))
+
+    for events, what in (([None] + ev[1:], "event 0 is NULL"), (ev[:3] + [None], "event 3 is NULL"),
+                         ([ev[0], ev[1], ev[0], ev[3]], "events 0 and 2 are the same")):
+        b = bufs(events)
+        assert L.zero_offload_step(ctypes.byref(src), 64, 1.0, h, hm, hv, ctypes.byref(hp), fake + (4 << 20),
+                                   Z.ZERO_BF16, ctypes.byref(b), None) == 1, what
+        assert what in Z.zero_last_error(), (what, Z.zero_last_error())
+    assert ctypes.sizeof(Z.ZeroOffloadBuffers) == 8 * 3 + 8 + 4 + 4 + 8 + 4 * 8

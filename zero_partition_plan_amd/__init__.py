@@ -80,7 +80,8 @@ class ZeroStageChoice(ctypes.Structure):
 class ZeroOffloadBuffers(ctypes.Structure):
     _fields_ = [("d_grad", ctypes.c_void_p), ("h_grad", ctypes.c_void_p), ("h_param", ctypes.c_void_p),
                 ("chunk_elems", ctypes.c_uint64), ("threads", ctypes.c_uint32),
-                ("reserved", ctypes.c_uint32), ("h2d_stream", ctypes.c_void_p)]
+                ("reserved", ctypes.c_uint32), ("h2d_stream", ctypes.c_void_p),
+                ("events", ctypes.c_void_p * 4)]
 
 
 class ZeroArenaArray(ctypes.Structure):
@@ -516,12 +517,17 @@ def zero_host_adam_step(grad, n: int, grad_scale: float, master, m, v, hp: ZeroA
 
 
 def offload_buffers(chunk_elems: int, device="cuda", threads: int = 0, h2d_stream=None) -> dict:
-    """Caller-side staging for zero_offload_step: device and pinned host chunk buffers (x2)."""
+    """Caller-side staging for zero_offload_step: device and pinned host chunk buffers (x2) and
+    the four events the step records and waits on (torch events, created here by recording each
+    once)."""
+    events = [torch.cuda.Event(enable_timing=False) for _ in range(4)]
+    for ev in events:
+        ev.record()                    # torch creates an event's handle on its first record
     bufs = {
         "d_grad": torch.empty(2 * chunk_elems, dtype=torch.float32, device=device),
         "h_grad": torch.empty(2 * chunk_elems, dtype=torch.float32, pin_memory=True),
         "h_param": torch.empty(2 * chunk_elems, dtype=torch.int16, pin_memory=True),
-        "chunk_elems": chunk_elems, "threads": threads, "h2d_stream": h2d_stream,
+        "chunk_elems": chunk_elems, "threads": threads, "h2d_stream": h2d_stream, "events": events,
     }
     return bufs
 
@@ -536,7 +542,8 @@ def zero_offload_step(reps, n: int, grad_scale: float, h_master, h_m, h_v, hp: Z
     b = ZeroOffloadBuffers(_ptr(buffers["d_grad"], 2 * C, "d_grad", (torch.float32,)),
                            _hptr(buffers["h_grad"], 2 * C, "h_grad", 4),
                            _hptr(buffers["h_param"], 2 * C, "h_param", 2), C, int(buffers["threads"]), 0,
-                           None if buffers.get("h2d_stream") is None else _stream(buffers["h2d_stream"]))
+                           None if buffers.get("h2d_stream") is None else _stream(buffers["h2d_stream"]),
+                           (ctypes.c_void_p * 4)(*[ev.cuda_event for ev in buffers["events"]]))
     _check(lib().zero_offload_step(
         ctypes.byref(src), n, float(grad_scale), _hptr(h_master, n, "master", 4), _hptr(h_m, n, "m", 4),
         _hptr(h_v, n, "v", 4), ctypes.byref(hp), _ptr(out, n, "out"), _TORCH_DT[out.dtype],

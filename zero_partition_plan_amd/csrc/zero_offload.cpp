@@ -30,6 +30,12 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
   if (!d_out_param) return zero::fail(ZERO_E_INVAL, "%s: the parameter slot is NULL", fn);
   if (!buf->d_grad || !buf->h_grad || !buf->h_param || buf->chunk_elems == 0)
     return zero::fail(ZERO_E_INVAL, "%s: incomplete staging buffers", fn);
+  for (int a = 0; a < 4; ++a) {
+    if (!buf->events[a]) return zero::fail(ZERO_E_INVAL, "%s: event %d is NULL", fn, a);
+    for (int b = 0; b < a; ++b)
+      if (buf->events[a] == buf->events[b])
+        return zero::fail(ZERO_E_INVAL, "%s: events %d and %d are the same", fn, b, a);
+  }
   const uint64_t C = buf->chunk_elems;
   if (C > UINT64_MAX / 16) return zero::fail(ZERO_E_OVERFLOW, "%s: chunk too large", fn);
   const int rb = (int)zero::dtype_bytes(src->dtype);
@@ -46,12 +52,10 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
 
   hipStream_t main = static_cast<hipStream_t>(stream);
   hipStream_t back = buf->h2d_stream ? static_cast<hipStream_t>(buf->h2d_stream) : main;
-  hipEvent_t got[2] = {nullptr, nullptr}, sent[2] = {nullptr, nullptr};
+  // the caller's events: a chunk's gradient has arrived (got), its parameters have left (sent)
+  hipEvent_t got[2] = {static_cast<hipEvent_t>(buf->events[0]), static_cast<hipEvent_t>(buf->events[1])};
+  hipEvent_t sent[2] = {static_cast<hipEvent_t>(buf->events[2]), static_cast<hipEvent_t>(buf->events[3])};
   hipError_t e = hipSuccess;
-  for (int b = 0; b < 2 && e == hipSuccess; ++b) {
-    e = hipEventCreateWithFlags(&got[b], hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&sent[b], hipEventDisableTiming);
-  }
   const bool l2 = hp->wd_mode == ZERO_ADAM_L2;
   const uint64_t nchunks = (n + C - 1) / C;
   // one team of host threads for every chunk of this call (threads that cannot start are left out)
@@ -103,10 +107,6 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
     // parameter copy from h_param), so that no copy touches the caller's host buffers after return
     (void)hipStreamSynchronize(main);
     if (back != main) (void)hipStreamSynchronize(back);
-  }
-  for (int b = 0; b < 2; ++b) {
-    if (got[b]) (void)hipEventDestroy(got[b]);
-    if (sent[b]) (void)hipEventDestroy(sent[b]);
   }
   if (s != ZERO_OK) return s;
   if (e != hipSuccess) return zero::fail(ZERO_E_HIP, "%s: %s", fn, hipGetErrorString(e));

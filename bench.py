@@ -1059,6 +1059,10 @@ def main(argv=None):
         log(f"{k}: {len(xs)} launches, avg {per_kernel[k]['avg_ms']:.4f} ms, median "
             f"{per_kernel[k]['median_ms']:.4f}, min {per_kernel[k]['min_ms']:.4f}, p90 "
             f"{per_kernel[k]['p90_ms']:.4f} -> {per_kernel[k]['gbs_at_avg']:.0f} GB/s")
+        if len(xs) >= 200:             # drift over a long timed region (clocks, temperature)
+            q = len(xs) // 10
+            log(f"{k}: first {q} launches avg {sum(xs[:q]) / q:.4f} ms, last {q} avg "
+                f"{sum(xs[-q:]) / q:.4f} ms")
     if "skipped" in st:
         log(f"overflow-skipped steps: {st['skipped']} of {args.warmup + args.steps}")
         xs = spans.ms("k_adam_step_skipped")

@@ -112,11 +112,15 @@ def test_reduce_sqnorm_skip_graph_replays_match_eager(device_clip):
             assert 0.0 < coef < 1.0                     # clipping is active
 
 
-def test_clipped_step_with_device_counter_replays_as_successive_steps():
+@pytest.mark.parametrize("static", [False, True])
+def test_clipped_step_with_device_counter_replays_as_successive_steps(static):
     """The whole clipped two-pass step (flag fill, reduce, squared norm, clip scale, update with t
     from a device counter, t advance) captured once: each replay is the next training step. Replays
     match eager steps with t from the host, bit for bit; an overflow written into a replica between
-    replays makes that replay skip, with t not advancing."""
+    replays makes that replay skip, with t not advancing. With ``static`` the captured step's
+    reduce and norm are zero_reduce_shard_static (no workspace; the partials in the library's own
+    scratch), which is what a caller that cannot allocate captures; the eager steps keep the
+    workspace pair."""
     n, R, ls = 256 * 700 + 9, 16, 2.0 ** 16
     g = torch.Generator(device=DEV)
     g.manual_seed(4)
@@ -135,14 +139,17 @@ def test_clipped_step_with_device_counter_replays_as_successive_steps():
                     status=torch.zeros(1, dtype=torch.int32, device=DEV),
                     out=torch.zeros(n, dtype=torch.float16, device=DEV))
 
-    def front(b):
+    def front(b, use_static=False):
         b["flag"].fill_(0)
-        Z.zero_reduce_shard(reps, n, b["g"], b["flag"], b["parts"], 1.0 / ls)
-        Z.zero_shard_sqnorm(None, n, 1.0 / ls, b["parts"], b["sq"])
+        if use_static:
+            Z.zero_reduce_shard_static(reps, n, b["g"], b["flag"], b["sq"], 1.0 / ls)
+        else:
+            Z.zero_reduce_shard(reps, n, b["g"], b["flag"], b["parts"], 1.0 / ls)
+            Z.zero_shard_sqnorm(None, n, 1.0 / ls, b["parts"], b["sq"])
         Z.zero_clip_scale(b["sq"], 0.01, 1e-6, 1.0 / ls, b["gs"])
 
     def graph_step(b):
-        front(b)
+        front(b, static)
         Z.zero_adam_shard_step_dev_t([b["g"]], n, b["gs"], table, b["t"], b["status"], b["p"], b["m"],
                                      b["v"], out=b["out"], skip=b["flag"])
 

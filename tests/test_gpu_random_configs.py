@@ -25,7 +25,7 @@ from gpu_util import DEV, assert_bits_equal, banner, bits16, bits32, dev_f32, de
 
 pytestmark = pytest.mark.gpu
 
-CASES = 60
+CASES = 300
 _T16 = {"bf16": torch.bfloat16, "f16": torch.float16}
 
 

@@ -4,8 +4,9 @@
  * back between its calls (zero_shard_sqnorm, zero_clip_scale, zero_adam_shard_step_dev_scale):
  * the device's grad scale must equal C's own double evaluation of the clip rule on the device's
  * norm, and the update must equal the host update with that scale; so must the same update with
- * t on the device (zero_adam_shard_step_dev_t), which also advances the counter. Exits 0 when all
- * match. */
+ * t on the device (zero_adam_shard_step_dev_t), which also advances the counter. Last, the reduce
+ * pass with no workspace (zero_reduce_shard_static) against the one with a caller's partials.
+ * Exits 0 when all match. */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -51,7 +52,8 @@ static uint16_t bf16_trunc(float x) { /* an input recipe: replicas as truncated 
 
 int main(void) {
   static uint16_t reps[R][N], out_dev[N], out_host[N];
-  static float p0[N], m0[N], v0[N], p_dev[N], m_dev[N], v_dev[N], p_host[N], m_host[N], v_host[N], g[N];
+  static float p0[N], m0[N], v0[N], p_dev[N], m_dev[N], v_dev[N], p_host[N], m_host[N], v_host[N], g[N],
+      g2[N];
   void* d_reps[R];
   const void* d_rep_ptrs[R];
   float *d_p, *d_m, *d_v, *d_g;
@@ -199,6 +201,38 @@ int main(void) {
       HIP(hipFree(d_table));
       HIP(hipFree(d_t));
       HIP(hipFree(d_status));
+    }
+
+    /* the reduce pass and its norm with no workspace (zero_reduce_shard_static, the partials in
+     * the library's own scratch) against zero_reduce_shard and zero_shard_sqnorm with a caller's
+     * partials: the gradient and the norm bit for bit, twice in a row */
+    {
+      double sq_ws, sq_static;
+      int32_t *d_flag, flag = -1;
+      float* d_g2;
+      int rep_i;
+      HIP(hipMalloc((void**)&d_flag, 4));
+      HIP(hipMalloc((void**)&d_g2, N * 4));
+      ZS(zero_reduce_shard(&src, N, NULL, NULL, d_parts, 0.25, NULL));
+      ZS(zero_shard_sqnorm(NULL, N, 0.25, d_parts, d_sq, NULL));
+      HIP(hipDeviceSynchronize());
+      HIP(hipMemcpy(&sq_ws, d_sq, 8, hipMemcpyDeviceToHost));
+      for (rep_i = 0; rep_i < 2; ++rep_i) {
+        HIP(hipMemset(d_flag, 0, 4));
+        HIP(hipMemset(d_sq, 0, 8));
+        ZS(zero_reduce_shard_static(&src, N, d_g2, d_flag, 0.25, d_sq, NULL));
+        HIP(hipDeviceSynchronize());
+        HIP(hipMemcpy(&sq_static, d_sq, 8, hipMemcpyDeviceToHost));
+        HIP(hipMemcpy(&flag, d_flag, 4, hipMemcpyDeviceToHost));
+        HIP(hipMemcpy(g2, d_g2, N * 4, hipMemcpyDeviceToHost));
+        if (memcmp(&sq_ws, &sq_static, 8) || flag != 0 || memcmp(g, g2, sizeof g)) {
+          fprintf(stderr, "static reduce: norm %.17g against %.17g, flag %d, gradient %s\n", sq_static,
+                  sq_ws, (int)flag, memcmp(g, g2, sizeof g) ? "differs" : "equal");
+          ++bad;
+        }
+      }
+      HIP(hipFree(d_flag));
+      HIP(hipFree(d_g2));
     }
     HIP(hipFree(d_parts));
     HIP(hipFree(d_sq));

@@ -26,8 +26,9 @@ Prints one JSON line (see the fields below). Flags:
                    command untraced, and exit
 
 The kernel-trace summary and the two counter passes (FETCH_SIZE, then WRITE_SIZE) are taken by the
-commands --profile-commands prints; their CSVs land in gpurun_out/prof_<workload>_{trace,fetch,write}
-and their console output in the .log file of the same name. The untraced run (prof_<workload>_plain.log)
+commands --profile-commands prints; their CSVs land in <root>/prof_<workload>_{trace,fetch,write}
+and their console output in the .log file of the same name, where <root> is $ZERO_PROFILE_ROOT
+(default profile_runs, relative to the repository root). The untraced run (prof_<workload>_plain.log)
 gives the event figure without the profiler's per-dispatch cost, for comparison in the summary.
 """
 
@@ -204,8 +205,13 @@ def recorded_traffic(workload: str, kernel: str):
 
 # ----------------------------------------------------------------------------- profiles
 
+def profile_root() -> str:
+    """Where the profiling commands write their output ($ZERO_PROFILE_ROOT, default profile_runs)."""
+    return os.environ.get("ZERO_PROFILE_ROOT", "profile_runs")
+
+
 def profile_dirs(workload: str) -> dict:
-    return {k: os.path.join("gpurun_out", f"prof_{workload}_{k}")
+    return {k: os.path.join(profile_root(), f"prof_{workload}_{k}")
             for k in ("trace", "fetch", "write", "plain")}
 
 

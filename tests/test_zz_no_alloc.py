@@ -77,3 +77,23 @@ def test_static_scratch_flag_and_norm_only():
         assert int(flag.item()) == int(bad)
         a, b = float(sq.item()), float(sq_w.item())
         assert (a == b) or (np.isnan(a) and np.isnan(b)) or (np.isinf(a) and a == b)
+
+
+def test_static_scratch_edges():
+    """An empty shard writes a zero norm; a call that asks for no norm uses no scratch and still
+    gives the gradient; a ragged size shorter than one tile; each checked against the workspace
+    pair."""
+    rng = np.random.default_rng(9)
+    reps = _reps(rng, 5, 77, "bf16", 1.0)
+    d_reps = [dev_rep(r, "bf16") for r in reps]
+    sq = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+    Z.zero_reduce_shard_static(d_reps, 0, None, None, sq, 1.0)
+    torch.cuda.synchronize()
+    assert float(sq.item()) == 0.0
+    g = torch.full((77,), float("nan"), device=DEV)
+    Z.zero_reduce_shard_static(d_reps, 77, g, None, None, 1.0)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits32(g), f32_bits(O.replica_sum(list(reps), "bf16")), "gradient without a norm")
+    (g_s, f_s, sq_s), (g_w, f_w, sq_w) = _both(d_reps, 77, 1.0)
+    assert_bits_equal(g_s, g_w, "ragged gradient")
+    assert sq_s == sq_w and f_s == f_w == 0

@@ -617,7 +617,7 @@ def gather_prefetch_context(st, tokens: int = 1024, reps: int = 3):
                     "then computing; a gather arriving over xGMI would load local HBM far less"}
 
 
-def setup_offload():
+def setup_offload(direct: bool = False):
     import torch
 
     import zero_partition_plan_amd as Z
@@ -633,10 +633,11 @@ def setup_offload():
     host = {k: inp[k].cpu().numpy() for k in ("master", "m", "v")}   # the state lives on the host
     del inp["master"], inp["m"], inp["v"]
     torch.cuda.empty_cache()
-    log(f"workload offload7b: S={S}, host state {3 * 4 * S / 1e9:.1f} GB, chunk {OFFLOAD_CHUNK}")
+    log(f"workload offload7b: S={S}, host state {3 * 4 * S / 1e9:.1f} GB, chunk {OFFLOAD_CHUNK}, "
+        f"staging {'direct' if direct else 'copy'}")
     st = dict(w=w, S=S, reps=inp["reps"], host=host, t=w.warm_steps + 1,
-              slot=torch.zeros(S, dtype=torch.bfloat16, device=dev),
-              bufs=Z.offload_buffers(OFFLOAD_CHUNK, threads=OFFLOAD_THREADS))
+              slot=torch.zeros(S, dtype=torch.bfloat16, device=dev), direct=direct,
+              bufs=Z.offload_buffers(OFFLOAD_CHUNK, threads=OFFLOAD_THREADS, direct=direct))
     torch.cuda.synchronize()
     return st
 
@@ -744,7 +745,9 @@ def copy_ceiling(gib: int = 4):
 
 
 def offload_parts(st):
-    """Rates of the offloaded step's parts measured alone: host update, D2H, H2D (one chunk)."""
+    """Rates of the offloaded step's parts measured alone: host update, D2H (by the copy engine and
+    by the reduce kernel writing host memory), H2D (one chunk); then whole steps with either
+    staging, interleaved."""
     import torch
 
     import zero_partition_plan_amd as Z
@@ -755,10 +758,11 @@ def offload_parts(st):
         Z.zero_host_adam_step(b["h_grad"], C, 1.0, h["master"][:C], h["m"][:C], h["v"][:C], hparams(st),
                               out=out, threads=OFFLOAD_THREADS)
     host_s = (time.perf_counter() - t0) / 3
+    d_src = b["d_grad"] if b["d_grad"] is not None else torch.empty(C, dtype=torch.float32, device="cuda")
     e0, e1 = new_event(), new_event()
     e0.record()
     for _ in range(3):
-        b["h_grad"][:C].copy_(b["d_grad"][:C], non_blocking=True)
+        b["h_grad"][:C].copy_(d_src[:C], non_blocking=True)
     e1.record()
     torch.cuda.synchronize()
     d2h_ms = e0.elapsed_time(e1) / 3
@@ -768,11 +772,38 @@ def offload_parts(st):
     e1.record()
     torch.cuda.synchronize()
     h2d_ms = e0.elapsed_time(e1) / 3
+    # the reduce kernel writing one chunk straight into pinned host memory
+    chunk = [r[:C] for r in st["reps"]]
+    h_g = b["h_grad"][:C]
+    Z.zero_reduce_shard(chunk, C, h_g)
+    e0.record()
+    for _ in range(3):
+        Z.zero_reduce_shard(chunk, C, h_g)
+    e1.record()
+    torch.cuda.synchronize()
+    kd2h_ms = e0.elapsed_time(e1) / 3
+    # whole steps with either staging, interleaved, on the same state
+    other = Z.offload_buffers(C, threads=OFFLOAD_THREADS, direct=not st["direct"])
+    both = {("direct" if st["direct"] else "copy"): b, ("copy" if st["direct"] else "direct"): other}
+    times = {k: [] for k in both}
+    for _ in range(4):
+        for k, bb in both.items():
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            Z.zero_offload_step(st["reps"], st["S"], 1.0, h["master"], h["m"], h["v"], hparams(st),
+                                st["slot"], bb)
+            times[k].append((time.perf_counter() - t0) * 1e3)
+            st["t"] += 1
+    del other
     return {"chunk_elems": C, "host_threads": OFFLOAD_THREADS,
             "host_update_gbs": 30 * C / host_s / 1e9, "host_update_params_per_s": C / host_s,
             "d2h_gbs": 4 * C / d2h_ms / 1e6, "h2d_gbs": 2 * C / h2d_ms / 1e6,
+            "d2h_by_kernel_gbs": 4 * C / kd2h_ms / 1e6,
+            "step_ms_by_staging": {k: round(sorted(v)[len(v) // 2], 2) for k, v in times.items()},
             "note": "host update moves 30 B per element in host memory (grad 4 + state 12 read, "
-                    "state 12 + bf16 2 written); d2h copies the fp32 gradient, h2d the bf16 parameters"}
+                    "state 12 + bf16 2 written); d2h copies the fp32 gradient, h2d the bf16 parameters; "
+                    "d2h_by_kernel: the reduce kernel writes the chunk into pinned host memory itself; "
+                    "step_ms_by_staging: the upper median of 4 whole steps each, interleaved"}
 
 
 def hparams(st):
@@ -963,6 +994,9 @@ def main(argv=None):
                     help="skip the context legs (copy ceiling, separate-placement step, cold launches, graph "
                          "replay), "
                          "so that a profiler sees only the timed step's launches")
+    ap.add_argument("--offload-staging", default="copy", choices=["copy", "direct"],
+                    help="offload7b: gradient chunks reduced into device staging and copied to pinned "
+                         "host memory, or written there by the reduce kernel itself")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle's CPU baseline (0 skips it)")
     ap.add_argument("--copy-calib", type=int, default=0,
@@ -1001,7 +1035,7 @@ def main(argv=None):
     if args.workload == "gather7b":
         st, step = setup_gather(), step_gather
     elif args.workload == "offload7b":
-        st, step = setup_offload(), step_offload
+        st, step = setup_offload(args.offload_staging == "direct"), step_offload
     else:
         st = setup(args.workload, args.placement)
         step = step_two_pass if args.workload.startswith("llama13b") else step_fused
@@ -1045,6 +1079,8 @@ def main(argv=None):
         # the reduce kernel runs inside the offloaded call; time it alone on one chunk
         import zero_partition_plan_amd as Z
         d_g = st["bufs"]["d_grad"]
+        if d_g is None:                    # direct staging: time the kernel into device memory here
+            d_g = torch.empty(OFFLOAD_CHUNK, dtype=torch.float32, device="cuda")
         chunk = [r[:OFFLOAD_CHUNK] for r in st["reps"]]      # built outside the timed spans
         for _ in range(2):
             Z.zero_reduce_shard(chunk, OFFLOAD_CHUNK, d_g)

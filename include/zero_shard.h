@@ -360,8 +360,11 @@ zero_status zero_host_adam_step(const float* grad, uint64_t n, float grad_scale,
 
 /* Staging for zero_offload_step, allocated by the caller. */
 typedef struct {
-  float* d_grad;        /* device float[2 * chunk_elems]: reduced-gradient chunks */
-  float* h_grad;        /* pinned host float[2 * chunk_elems]: their copies */
+  float* d_grad;        /* device float[2 * chunk_elems]: reduced-gradient chunks, or NULL: the
+                           reduce kernel then writes each chunk straight into h_grad over the host
+                           link, with no device staging and no copy */
+  float* h_grad;        /* pinned host float[2 * chunk_elems] (hipHostMalloc, so that the device can
+                           write it): the chunks the host updates from */
   void* h_param;        /* pinned host 16-bit [2 * chunk_elems]: updated parameters */
   uint64_t chunk_elems; /* pipeline chunk, >= 1 */
   uint32_t threads;     /* host threads for the update (0 = all) */
@@ -372,7 +375,8 @@ typedef struct {
 } zero_offload_buffers;
 
 /* One rank's offloaded step (P2 ZeRO-Offload): for each chunk of the shard, the GPU sums the
- * gradient replicas (as zero_reduce_shard) and the chunk is copied to pinned host memory; the host
+ * gradient replicas (as zero_reduce_shard) and the chunk reaches pinned host memory (copied from
+ * the device staging, or written there by the kernel when d_grad is NULL); the host
  * runs zero_host_adam_step on its part of h_master/h_m/h_v (host float[n], updated in place) and
  * the 16-bit parameters are copied into d_out_param (device, the rank's slot, out_dtype bf16 or
  * fp16). Chunks are double-buffered: the GPU reduces and copies chunk c+1 while the host updates
@@ -381,8 +385,8 @@ typedef struct {
  * copy has landed. It allocates nothing and creates no HIP objects (the staging and the events are
  * the caller's); its host threads are started once per call and serve every chunk. Aliasing:
  * d_out_param, the staging d_grad and the replicas must not overlap. Errors: as zero_host_adam_step
- * and zero_reduce_shard, plus NULL or incomplete buffers (a NULL or repeated event) or device
- * aliasing -> ZERO_E_INVAL and HIP failures -> ZERO_E_HIP (the state may then be partly updated). */
+ * and zero_reduce_shard, plus NULL or incomplete buffers (h_grad or h_param NULL, chunk_elems 0, a
+ * NULL or repeated event) or device aliasing -> ZERO_E_INVAL and HIP failures -> ZERO_E_HIP (the state may then be partly updated). */
 zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_scale,
                               float* h_master, float* h_m, float* h_v, const zero_adam_hparams* hp,
                               void* d_out_param, int32_t out_dtype,

@@ -556,3 +556,26 @@ def test_offload_step_needs_four_distinct_events():
                                    Z.ZERO_BF16, ctypes.byref(b), None) == 1, what
         assert what in Z.zero_last_error(), (what, Z.zero_last_error())
     assert ctypes.sizeof(Z.ZeroOffloadBuffers) == 8 * 3 + 8 + 4 + 4 + 8 + 4 * 8
+
+
+def test_offload_direct_staging_checks():
+    """With no device staging (d_grad NULL) the reduce kernel writes the pinned host chunks
+    itself, so those are what is checked against the slot and the replicas; a NULL h_grad is
+    still refused. All refused before any device work."""
+    L = Z.lib()
+    fake = 1 << 40                                   # never dereferenced: every call below is invalid
+    hp = Z.adam_hparams()
+    src, keep = _src([fake], Z.ZERO_BF16)
+    h = (ctypes.c_float * 64)()
+    hm, hv = (ctypes.c_float * 64)(), (ctypes.c_float * 64)()
+    ev = (ctypes.c_void_p * 4)(fake + 0x100, fake + 0x200, fake + 0x300, fake + 0x400)
+    slot = fake + (4 << 20)
+
+    def call(h_grad, out=slot):
+        b = Z.ZeroOffloadBuffers(None, h_grad, fake + (3 << 20), 16, 1, 0, None, ev)
+        return L.zero_offload_step(ctypes.byref(src), 64, 1.0, h, hm, hv, ctypes.byref(hp), out,
+                                   Z.ZERO_BF16, ctypes.byref(b), None)
+
+    assert call(None) == 1 and "incomplete staging buffers" in Z.zero_last_error()
+    assert call(slot + 100) == 1 and "the slot overlaps the gradient staging" in Z.zero_last_error()
+    assert call(fake + 64) == 1 and "the gradient staging overlaps replica 0" in Z.zero_last_error()

@@ -1,6 +1,7 @@
 """GPU + host parity of the offloaded step (ZeRO-Offload): device replica sum per chunk, copy to
-pinned host memory, host Adam on host state, 16-bit parameters copied into the device slot. Bit
-for bit against the oracle and against the all-device step on the same inputs."""
+pinned host memory (or the reduce kernel writing there itself, with no device staging), host Adam
+on host state, 16-bit parameters copied into the device slot. Bit for bit against the oracle and
+against the all-device step on the same inputs."""
 
 import numpy as np
 import pytest
@@ -24,11 +25,13 @@ def _inputs(rng, n, R):
     return reps, master, m, v
 
 
-@pytest.mark.parametrize("n,chunk,side", [(5 * 4096 + 777, 4096, False), (5 * 4096 + 777, 4096, True),
-                                          (1000, 4096, False), (1, 1, True), (3 * 65536, 65536, True),
-                                          (64 << 20, 8 << 20, True)])
-def test_offload_step_matches_oracle_and_device_step(n, chunk, side):
-    banner(f"offload n={n} chunk={chunk} side={side}")
+@pytest.mark.parametrize("n,chunk,side,direct", [
+    (5 * 4096 + 777, 4096, False, False), (5 * 4096 + 777, 4096, True, False),
+    (1000, 4096, False, False), (1, 1, True, False), (3 * 65536, 65536, True, False),
+    (64 << 20, 8 << 20, True, False),
+    (5 * 4096 + 777, 4096, False, True), (1, 1, True, True), (64 << 20, 8 << 20, True, True)])
+def test_offload_step_matches_oracle_and_device_step(n, chunk, side, direct):
+    banner(f"offload n={n} chunk={chunk} side={side} direct={direct}")
     rng = np.random.default_rng(n % 997 + chunk)
     R = 8
     reps, master, m, v = _inputs(rng, n, R)
@@ -38,7 +41,8 @@ def test_offload_step_matches_oracle_and_device_step(n, chunk, side):
     hm, hmm, hv = master.copy(), m.copy(), v.copy()
     slot = torch.full((n + 8,), -1.0, dtype=torch.bfloat16, device=DEV)
     stream = torch.cuda.Stream() if side else None
-    bufs = Z.offload_buffers(chunk, threads=8, h2d_stream=stream)
+    bufs = Z.offload_buffers(chunk, threads=8, h2d_stream=stream, direct=direct)
+    assert (bufs["d_grad"] is None) == direct
     Z.zero_offload_step(d_reps, n, 0.5, hm, hmm, hv, hp, slot[4:4 + n], bufs)
     torch.cuda.synchronize()
     got_slot = bits16(slot)
@@ -92,7 +96,8 @@ def test_offload_rejects_bad_buffers():
 @pytest.mark.parametrize("seed", range(12))
 def test_offload_random_configurations(seed):
     """Seeded random sizes, chunk sizes (also larger than the shard), host thread counts, replica
-    counts and dtypes, output dtypes, decay modes and copy-back streams, against the oracle."""
+    counts and dtypes, output dtypes, decay modes, copy-back streams and staging (device buffer
+    and copy, or the kernel writing host memory), against the oracle."""
     rng = np.random.default_rng(40_000 + seed)
     n = int(rng.choice([rng.integers(1, 2000), rng.integers(2000, 300_000)]))
     chunk = int(rng.choice([1, 7, 256, 4096, 65536, 1 << 20]))
@@ -115,10 +120,13 @@ def test_offload_random_configurations(seed):
     m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
     v = (rng.random(n) * 1e-7).astype(np.float32)
     kw = {**HP, "wd_mode": mode, "step": int(rng.integers(1, 100))}
+    direct = bool(rng.integers(0, 2))
+    banner(f"  staging: {'kernel writes host memory' if direct else 'device buffer + copy'}")
     hm, hmm, hv = master.copy(), m.copy(), v.copy()
     t16 = torch.bfloat16 if odt == "bf16" else torch.float16
     slot = torch.full((n + 6,), -1.0, dtype=t16, device=DEV)
-    bufs = Z.offload_buffers(chunk, threads=threads, h2d_stream=torch.cuda.Stream() if side else None)
+    bufs = Z.offload_buffers(chunk, threads=threads, h2d_stream=torch.cuda.Stream() if side else None,
+                             direct=direct)
     Z.zero_offload_step(d_reps, n, 0.25, hm, hmm, hv, Z.adam_hparams(**kw), slot[3:3 + n], bufs)
     torch.cuda.synchronize()
     p2, m2, v2, o2 = O.sharded_step(list(reps), rdt, 0.25, master, m, v, O.AdamHParams(**kw), odt)
@@ -128,3 +136,22 @@ def test_offload_random_configurations(seed):
     got = bits16(slot)
     assert (got[:3] == got[0]).all() and (got[3 + n:] == got[0]).all(), "write outside the slot"
     assert_bits_equal(got[3:3 + n], o2, "slot")
+
+
+def test_reduce_into_pinned_host_memory():
+    """The reduce pass writing straight into pinned host memory (the offloaded step's direct
+    staging) gives the bits it gives into device memory, over several tiles and a ragged tail;
+    a plain (pageable) host tensor is refused by the binding."""
+    rng = np.random.default_rng(77)
+    n, R = 3 * 4096 + 123, 5
+    reps, _, _, _ = _inputs(rng, n, R)
+    d_reps = [dev_rep(r, "bf16") for r in reps]
+    h = torch.full((n,), float("nan"), dtype=torch.float32, pin_memory=True)
+    d = torch.empty(n, dtype=torch.float32, device=DEV)
+    Z.zero_reduce_shard(d_reps, n, h)
+    Z.zero_reduce_shard(d_reps, n, d)
+    torch.cuda.synchronize()
+    assert_bits_equal(h.numpy().view(np.uint32), bits32(d), "pinned vs device")
+    assert_bits_equal(h.numpy().view(np.uint32), f32_bits(O.replica_sum(list(reps), "bf16")), "pinned vs oracle")
+    with pytest.raises(TypeError):
+        Z.zero_reduce_shard(d_reps, n, torch.empty(n, dtype=torch.float32))

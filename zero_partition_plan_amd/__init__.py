@@ -301,11 +301,11 @@ def arena(specs, device="cuda", contiguous: bool = True):
 
 # ------------------------------------------------------------------------------ device calls
 
-def _ptr(t, n: int, what: str, dtype=None) -> int | None:
+def _ptr(t, n: int, what: str, dtype=None, pinned_ok: bool = False) -> int | None:
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{what} must be a device tensor")
+    if not isinstance(t, torch.Tensor) or not (t.is_cuda or (pinned_ok and t.is_pinned())):
+        raise TypeError(f"{what} must be a device tensor" + (" or pinned host memory" if pinned_ok else ""))
     if dtype is not None and t.dtype not in dtype:
         raise TypeError(f"{what}: dtype {t.dtype} not in {dtype}")
     if not t.is_contiguous():
@@ -340,9 +340,10 @@ def zero_sq_partials_len(n: int) -> int:
 
 def zero_reduce_shard(reps, n: int, out_grad=None, nonfinite=None, sq_partials=None,
                       sq_scale: float = 1.0, stream=None):
+    """``out_grad`` may also be pinned host memory, which the kernel then writes over the host link."""
     src, keep = _src(reps, n)
     _check(lib().zero_reduce_shard(
-        ctypes.byref(src), n, _ptr(out_grad, n, "out_grad", (torch.float32,)),
+        ctypes.byref(src), n, _ptr(out_grad, n, "out_grad", (torch.float32,), pinned_ok=True),
         _ptr(nonfinite, 1, "nonfinite", (torch.int32,)),
         _ptr(sq_partials, zero_sq_partials_len(n), "sq_partials", (torch.float64,)),
         float(sq_scale), _stream(stream)), "zero_reduce_shard")
@@ -516,15 +517,17 @@ def zero_host_adam_step(grad, n: int, grad_scale: float, master, m, v, hp: ZeroA
         out_dtype, threads), "zero_host_adam_step")
 
 
-def offload_buffers(chunk_elems: int, device="cuda", threads: int = 0, h2d_stream=None) -> dict:
+def offload_buffers(chunk_elems: int, device="cuda", threads: int = 0, h2d_stream=None,
+                    direct: bool = False) -> dict:
     """Caller-side staging for zero_offload_step: device and pinned host chunk buffers (x2) and
     the four events the step records and waits on (torch events, created here by recording each
-    once)."""
+    once). ``direct``: no device staging; the reduce kernel writes each chunk into the pinned host
+    buffer itself."""
     events = [torch.cuda.Event(enable_timing=False) for _ in range(4)]
     for ev in events:
         ev.record()                    # torch creates an event's handle on its first record
     bufs = {
-        "d_grad": torch.empty(2 * chunk_elems, dtype=torch.float32, device=device),
+        "d_grad": None if direct else torch.empty(2 * chunk_elems, dtype=torch.float32, device=device),
         "h_grad": torch.empty(2 * chunk_elems, dtype=torch.float32, pin_memory=True),
         "h_param": torch.empty(2 * chunk_elems, dtype=torch.int16, pin_memory=True),
         "chunk_elems": chunk_elems, "threads": threads, "h2d_stream": h2d_stream, "events": events,

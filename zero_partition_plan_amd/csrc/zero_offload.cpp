@@ -3,10 +3,11 @@
 // GPU, and a pipeline keeps CPU and GPU working at once).
 //
 // zero_offload_step runs the whole offloaded step for a rank's shard in chunks, double-buffered:
-// the GPU sums the gradient replicas of chunk c+1 and copies it to pinned host memory while the
-// host updates chunk c (zero_host_adam.cpp), and chunk c's 16-bit parameters are copied back to
-// the rank's slot on a second stream while the host works on chunk c+1. The host threads are
-// started once per call and serve every chunk.
+// the GPU sums the gradient replicas of chunk c+1 and copies it to pinned host memory (or, with no
+// device staging, the reduce kernel writes it there itself) while the host updates chunk c
+// (zero_host_adam.cpp), and chunk c's 16-bit parameters are copied back to the rank's slot on a
+// second stream while the host works on chunk c+1. The host threads are started once per call and
+// serve every chunk.
 #include <hip/hip_runtime_api.h>
 
 #include "zero_host_adam.h"
@@ -28,7 +29,7 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
   if (!src || !buf) return zero::fail(ZERO_E_INVAL, "%s: NULL source or buffers", fn);
   if (n == 0) return zero::ok();
   if (!d_out_param) return zero::fail(ZERO_E_INVAL, "%s: the parameter slot is NULL", fn);
-  if (!buf->d_grad || !buf->h_grad || !buf->h_param || buf->chunk_elems == 0)
+  if (!buf->h_grad || !buf->h_param || buf->chunk_elems == 0)
     return zero::fail(ZERO_E_INVAL, "%s: incomplete staging buffers", fn);
   for (int a = 0; a < 4; ++a) {
     if (!buf->events[a]) return zero::fail(ZERO_E_INVAL, "%s: event %d is NULL", fn, a);
@@ -41,12 +42,15 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
   const int rb = (int)zero::dtype_bytes(src->dtype);
   if (!src->ptrs || src->count == 0 || src->count > ZERO_MAX_REPLICAS)
     return zero::fail(ZERO_E_INVAL, "%s: bad gradient source", fn);
-  if (zero::overlaps(d_out_param, n * 2, buf->d_grad, 2 * C * 4))
+  // where the reduce kernel writes: the device staging, else the pinned host chunks themselves
+  const bool direct = buf->d_grad == nullptr;
+  float* red = direct ? buf->h_grad : buf->d_grad;
+  if (zero::overlaps(d_out_param, n * 2, red, 2 * C * 4))
     return zero::fail(ZERO_E_INVAL, "%s: the slot overlaps the gradient staging", fn);
   for (uint32_t r = 0; r < src->count; ++r) {
     if (zero::overlaps(d_out_param, n * 2, src->ptrs[r], n * rb))
       return zero::fail(ZERO_E_INVAL, "%s: the slot overlaps replica %u", fn, r);
-    if (zero::overlaps(buf->d_grad, 2 * C * 4, src->ptrs[r], n * rb))
+    if (zero::overlaps(red, 2 * C * 4, src->ptrs[r], n * rb))
       return zero::fail(ZERO_E_INVAL, "%s: the gradient staging overlaps replica %u", fn, r);
   }
 
@@ -63,17 +67,20 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
   const void* ptrs[ZERO_MAX_REPLICAS];   // one chunk's replica pointers (no allocation)
   bool sent_any[2] = {false, false};
 
-  // enqueue chunk c on the GPU: replica sum into d_grad[b], copy to h_grad[b]
+  // enqueue chunk c on the GPU: replica sum into d_grad[b] and a copy to h_grad[b], or the sum
+  // straight into h_grad[b]
   auto issue = [&](uint64_t c) -> zero_status {
     const uint64_t off = c * C, len = n - off < C ? n - off : C;
     const int b = (int)(c & 1);
     for (uint32_t r = 0; r < src->count; ++r)
       ptrs[r] = static_cast<const char*>(src->ptrs[r]) + off * rb;
     const zero_grad_src part{ptrs, src->count, src->dtype};
-    zero_status rs = zero_reduce_shard(&part, len, buf->d_grad + b * C, nullptr, nullptr, 1.0, main);
+    zero_status rs = zero_reduce_shard(&part, len, red + b * C, nullptr, nullptr, 1.0, main);
     if (rs != ZERO_OK) return rs;
-    hipError_t ce = hipMemcpyAsync(buf->h_grad + b * C, buf->d_grad + b * C, len * 4,
-                                   hipMemcpyDeviceToHost, main);
+    hipError_t ce = hipSuccess;
+    if (!direct)
+      ce = hipMemcpyAsync(buf->h_grad + b * C, buf->d_grad + b * C, len * 4, hipMemcpyDeviceToHost,
+                          main);
     if (ce == hipSuccess) ce = hipEventRecord(got[b], main);
     if (ce != hipSuccess) return zero::fail(ZERO_E_HIP, "%s: %s", fn, hipGetErrorString(ce));
     return ZERO_OK;
@@ -103,8 +110,9 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
     if (sent_any[b] && e == hipSuccess) e = hipEventSynchronize(sent[b]);
   }
   if (e != hipSuccess || s != ZERO_OK) {
-    // after a failure, still wait for whatever was enqueued (a gradient copy into h_grad, a
-    // parameter copy from h_param), so that no copy touches the caller's host buffers after return
+    // after a failure, still wait for whatever was enqueued (a gradient copy or the reduce kernel
+    // writing h_grad, a parameter copy from h_param), so that nothing touches the caller's host
+    // buffers after return
     (void)hipStreamSynchronize(main);
     if (back != main) (void)hipStreamSynchronize(back);
   }

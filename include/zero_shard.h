@@ -351,7 +351,10 @@ zero_status zero_gather_params(const void* const* d_shards, uint32_t nd, uint64_
  * and rounding of zero_adam_shard_step (so both give the same bits), on the fp32 gradient grad
  * (host float[n]) times grad_scale; master, m, v (host float[n]) are updated in place and
  * out_param (host, nullable) receives the bf16/fp16 round-to-nearest-even parameters. threads: host
- * threads to split the range over (0 = all hardware threads). Synchronous; no HIP calls.
+ * threads to split the range over (0 = all hardware threads). On CPUs with AVX2 and F16C the
+ * results are written with streaming stores (to memory, not kept in the caches) when master, m and
+ * v share one 32-byte phase (the fastest layout: all three 32-byte aligned). Synchronous; no HIP
+ * calls.
  * Errors: NULLs, bad hparams, overlapping arrays -> ZERO_E_INVAL; out dtype fp32 ->
  * ZERO_E_UNSUPPORTED; n*8 >= 2^64 -> ZERO_E_OVERFLOW. */
 zero_status zero_host_adam_step(const float* grad, uint64_t n, float grad_scale, float* master,

@@ -138,3 +138,54 @@ def test_host_step_ieee_special_cases(case, threads):
         for got, want, what in ((p2, wp, "master"), (m2, wm, "m"), (v2, wv, "v")):
             assert_bits_equal_nan(got.view(np.uint32), want.view(np.uint32), f"{what} ({odt})")
         assert_bits_equal_nan(out, wo, f"out {odt}", odt)
+
+
+def _aligned(n, dtype, fill=0):
+    """n elements of dtype whose first element sits on a 64-byte boundary."""
+    item = np.dtype(dtype).itemsize
+    raw = np.full(n + 64 // item, fill, dtype)
+    k = (-raw.ctypes.data % 64) // item
+    a = raw[k:k + n]
+    assert a.ctypes.data % 64 == 0
+    return a
+
+
+@pytest.mark.parametrize("odt", ["bf16", "f16", None])
+@pytest.mark.parametrize("mode", ["adamw", "l2"])
+def test_host_step_array_phases(odt, mode):
+    """Master, m, v, the gradient and the 16-bit output each start at their own offset within a
+    32-byte line, so every form of the host loop runs: streamed state with a streamed or a plain
+    16-bit store (scalar head and tail around the vector body), and the plain loop when m or v is
+    out of master's phase. Bit for bit against the oracle, nothing written outside the arrays."""
+    rng = np.random.default_rng(hash((odt, mode)) % 1000)
+    hp = {**HP, "wd_mode": mode, "step": 3}
+    for n in (1, 7, 8, 9, 100, 4099, 70_001):
+        # (master, m, v, gradient, output) offsets in elements from 64-byte aligned bases: all on
+        # the boundary; a 5-element head with the output still streamed after it; a 7-element head
+        # leaving the output off its 16 bytes (plain 16-bit stores); v and then m out of master's
+        # phase (the plain loop)
+        for offs in ((0, 0, 0, 0, 0), (3, 3, 3, 5, 3), (1, 1, 1, 1, 7), (0, 0, 4, 0, 0), (5, 2, 5, 6, 1)):
+            op, om, ov, og, oo = offs
+            master, g, m, v = _case(rng, n)
+            P = _aligned(n + 16, np.float32); P[op:op + n] = master
+            M = _aligned(n + 16, np.float32); M[om:om + n] = m
+            V = _aligned(n + 16, np.float32); V[ov:ov + n] = v
+            G = _aligned(n + 16, np.float32); G[og:og + n] = g
+            out = _aligned(n + 16, np.uint16, 0x5A5A)
+            Z.zero_host_adam_step(G[og:og + n], n, 0.5, P[op:op + n], M[om:om + n], V[ov:ov + n],
+                                  Z.adam_hparams(**hp), out=out[oo:oo + n] if odt else None,
+                                  out_dtype={"bf16": Z.ZERO_BF16, "f16": Z.ZERO_F16, None: Z.ZERO_BF16}[odt],
+                                  threads=3)
+            wp, wm, wv, wo = O.sharded_step([g], "f32", 0.5, master, m, v, O.AdamHParams(**hp), odt)
+            what = (n, offs)
+            assert np.array_equal(P[op:op + n].view(np.uint32), wp.view(np.uint32)), what
+            assert np.array_equal(M[om:om + n].view(np.uint32), wm.view(np.uint32)), what
+            assert np.array_equal(V[ov:ov + n].view(np.uint32), wv.view(np.uint32)), what
+            for arr, o in ((P, op), (M, om), (V, ov)):
+                assert not arr[:o].any() and not arr[o + n:].any(), what
+            if odt:
+                assert np.array_equal(out[oo:oo + n], wo), what
+            keep = np.ones(n + 16, bool)
+            if odt:
+                keep[oo:oo + n] = False
+            assert (out[keep] == 0x5A5A).all(), what

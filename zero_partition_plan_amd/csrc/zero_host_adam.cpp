@@ -2,8 +2,12 @@
 // “分”着用", ZeRO-Offload: the CPU updates the optimizer state kept in host memory). The same fp32
 // operation order as the GPU kernel, each operation rounded on its own (built with
 // -ffp-contract=off; x86 division and square root are correctly rounded), so the two agree bit for
-// bit. The range is split over host threads; an AVX2 build of the loop is used when the CPU has it.
-// No HIP calls: this file also builds with a plain host compiler (and its sanitizers).
+// bit. The range is split over host threads. On CPUs with AVX2 and F16C the loop is written with
+// vector intrinsics and streaming (non-temporal) stores: the state and the 16-bit parameters go
+// straight to memory instead of being read for ownership into the caches, which the update, bound
+// by host memory, turns into time. No HIP calls: this file also builds with a plain host compiler
+// (and its sanitizers).
+#include <immintrin.h>
 #include <math.h>
 #include <string.h>
 
@@ -90,13 +94,91 @@ __attribute__((target("avx2"))) void range_avx2(const HostStep& s, uint64_t lo, 
   adam_range<L2, ODT>(s, lo, hi);
 }
 
+// Eight elements of the update in AVX2, the same operations in the same order as adam_range (each
+// IEEE-rounded on its own: vdivps and vsqrtps are correctly rounded, and nothing is contracted).
+// Master, m and v are loaded from and streamed to 32-byte aligned addresses; the gradient may sit
+// anywhere; the 16-bit parameters are streamed when OUT_NT (16-byte aligned) and stored plainly
+// otherwise.
+template <bool L2, int ODT, bool OUT_NT>
+__attribute__((target("avx2,f16c"))) inline void adam8_stream(const HostStep& s, uint64_t i) {
+  const zero_adam_scalars& k = s.k;
+  __m256 g = _mm256_mul_ps(_mm256_loadu_ps(s.g + i), _mm256_set1_ps(s.gs));
+  __m256 p = _mm256_load_ps(s.P + i), m = _mm256_load_ps(s.M + i), v = _mm256_load_ps(s.V + i);
+  if (L2) g = _mm256_add_ps(g, _mm256_mul_ps(_mm256_set1_ps(k.w), p));
+  m = _mm256_add_ps(_mm256_mul_ps(_mm256_set1_ps(k.b1), m), _mm256_mul_ps(_mm256_set1_ps(k.c1), g));
+  v = _mm256_add_ps(_mm256_mul_ps(_mm256_set1_ps(k.b2), v),
+                    _mm256_mul_ps(_mm256_set1_ps(k.c2), _mm256_mul_ps(g, g)));
+  const __m256 den = _mm256_add_ps(_mm256_div_ps(_mm256_sqrt_ps(v), _mm256_set1_ps(k.bc)),
+                                   _mm256_set1_ps(k.e));
+  if (!L2) p = _mm256_mul_ps(p, _mm256_set1_ps(k.dec));
+  p = _mm256_sub_ps(p, _mm256_mul_ps(_mm256_set1_ps(k.ss), _mm256_div_ps(m, den)));
+  _mm256_stream_ps(s.P + i, p);
+  _mm256_stream_ps(s.M + i, m);
+  _mm256_stream_ps(s.V + i, v);
+  if (ODT == ZERO_F32) return;
+  __m128i h;
+  if (ODT == ZERO_F16) {
+    // the hardware binary16 conversion rounds to nearest even, keeps subnormals, overflows to
+    // infinity and quiets a NaN keeping its top payload bits: f16_rne for every fp32 pattern
+    h = _mm256_cvtps_ph(p, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
+  } else {
+    // bf16_rne on eight lanes: NaN -> top half with the quiet bit, else add 0x7fff + lsb, shift
+    const __m256i u = _mm256_castps_si256(p);
+    const __m256i nan = _mm256_cmpgt_epi32(_mm256_and_si256(u, _mm256_set1_epi32(0x7fffffff)),
+                                           _mm256_set1_epi32(0x7f800000));
+    const __m256i lsb = _mm256_and_si256(_mm256_srli_epi32(u, 16), _mm256_set1_epi32(1));
+    const __m256i rne = _mm256_srli_epi32(
+        _mm256_add_epi32(u, _mm256_add_epi32(_mm256_set1_epi32(0x7fff), lsb)), 16);
+    const __m256i qn = _mm256_or_si256(_mm256_srli_epi32(u, 16), _mm256_set1_epi32(0x40));
+    const __m256i b = _mm256_blendv_epi8(rne, qn, nan);
+    h = _mm_packus_epi32(_mm256_castsi256_si128(b), _mm256_extracti128_si256(b, 1));
+  }
+  if (OUT_NT) _mm_stream_si128(reinterpret_cast<__m128i*>(s.out + i), h);
+  else _mm_storeu_si128(reinterpret_cast<__m128i*>(s.out + i), h);
+}
+
+template <bool L2, int ODT, bool OUT_NT>
+__attribute__((target("avx2,f16c"))) void stream_body(const HostStep& s, uint64_t i, uint64_t hi) {
+  for (; i + 8 <= hi; i += 8) adam8_stream<L2, ODT, OUT_NT>(s, i);
+  adam_range<L2, ODT>(s, i, hi);
+}
+
+// The streaming form over [lo, hi): a scalar head up to master's first 32-byte boundary, the
+// vector body, a scalar tail. When m or v does not share master's 32-byte phase the whole range
+// takes the plain AVX2 loop. Ends with a store fence: streaming stores are weakly ordered, and
+// the caller hands the results on (to another thread, or to a DMA copy) after this returns.
+template <bool L2, int ODT>
+__attribute__((target("avx2,f16c"))) void range_stream(const HostStep& s, uint64_t lo, uint64_t hi) {
+  const auto phase = [](const void* p) { return reinterpret_cast<uintptr_t>(p) & 31u; };
+  if (phase(s.M + lo) != phase(s.P + lo) || phase(s.V + lo) != phase(s.P + lo)) {
+    adam_range<L2, ODT>(s, lo, hi);
+    return;
+  }
+  uint64_t i = lo;
+  while (i < hi && phase(s.P + i) != 0) ++i;
+  adam_range<L2, ODT>(s, lo, i);
+  if (ODT != ZERO_F32 && (reinterpret_cast<uintptr_t>(s.out + i) & 15u) == 0)
+    stream_body<L2, ODT, true>(s, i, hi);
+  else
+    stream_body<L2, ODT, false>(s, i, hi);
+  _mm_sfence();
+}
+
 typedef zero::HostRangeFn RangeFn;
 
+enum class Isa { kBase, kAvx2, kStream };
+
+template <bool L2, int ODT>
+RangeFn pick_isa(Isa isa) {
+  if (isa == Isa::kStream) return range_stream<L2, ODT>;
+  return isa == Isa::kAvx2 ? range_avx2<L2, ODT> : range_base<L2, ODT>;
+}
+
 template <bool L2>
-RangeFn pick_odt(int odt, bool avx2) {
-  if (odt == ZERO_BF16) return avx2 ? range_avx2<L2, ZERO_BF16> : range_base<L2, ZERO_BF16>;
-  if (odt == ZERO_F16) return avx2 ? range_avx2<L2, ZERO_F16> : range_base<L2, ZERO_F16>;
-  return avx2 ? range_avx2<L2, ZERO_F32> : range_base<L2, ZERO_F32>;
+RangeFn pick_odt(int odt, Isa isa) {
+  if (odt == ZERO_BF16) return pick_isa<L2, ZERO_BF16>(isa);
+  if (odt == ZERO_F16) return pick_isa<L2, ZERO_F16>(isa);
+  return pick_isa<L2, ZERO_F32>(isa);
 }
 
 uint32_t hw_threads(uint32_t threads) {
@@ -142,9 +224,11 @@ void run_threads(RangeFn fn, const HostStep& s, uint64_t n, uint32_t threads) {
   for (auto& th : pool) th.join();
 }
 
-bool have_avx2() {
-  static const bool yes = __builtin_cpu_supports("avx2");
-  return yes;
+Isa host_isa() {
+  static const Isa isa = !__builtin_cpu_supports("avx2") ? Isa::kBase
+                         : __builtin_cpu_supports("f16c") ? Isa::kStream
+                                                          : Isa::kAvx2;
+  return isa;
 }
 
 }  // namespace
@@ -227,7 +311,7 @@ zero_status host_step(const float* grad, uint64_t n, float grad_scale, float* ma
                       uint32_t threads, HostTeam* team) {
   HostStep s{grad, grad_scale, master, m, v, static_cast<uint16_t*>(out), k};
   const int odt = out ? out_dtype : ZERO_F32;
-  const RangeFn fn = l2 ? pick_odt<true>(odt, have_avx2()) : pick_odt<false>(odt, have_avx2());
+  const RangeFn fn = l2 ? pick_odt<true>(odt, host_isa()) : pick_odt<false>(odt, host_isa());
   if (team != nullptr) team->run(fn, s, n);
   else run_threads(fn, s, n, threads);
   return ZERO_OK;

@@ -744,10 +744,11 @@ def copy_ceiling(gib: int = 4):
             "note": f"k_gather copying one contiguous {gib} GiB array (practical ceiling of a 1:1 copy)"}
 
 
-def offload_parts(st):
-    """Rates of the offloaded step's parts measured alone: host update, D2H (by the copy engine and
-    by the reduce kernel writing host memory), H2D (one chunk); then whole steps with either
-    staging, interleaved."""
+def offload_parts(st, context: bool = True):
+    """Rates of the offloaded step's parts measured alone: host update, D2H, H2D (one chunk); with
+    ``context``, also the reduce kernel writing a chunk into host memory and whole steps with either
+    staging, interleaved (these launch k_reduce at the host link's pace, so a profiled run skips
+    them)."""
     import torch
 
     import zero_partition_plan_amd as Z
@@ -772,6 +773,13 @@ def offload_parts(st):
     e1.record()
     torch.cuda.synchronize()
     h2d_ms = e0.elapsed_time(e1) / 3
+    parts = {"chunk_elems": C, "host_threads": OFFLOAD_THREADS,
+             "host_update_gbs": 30 * C / host_s / 1e9, "host_update_params_per_s": C / host_s,
+             "d2h_gbs": 4 * C / d2h_ms / 1e6, "h2d_gbs": 2 * C / h2d_ms / 1e6,
+             "note": "host update moves 30 B per element in host memory (grad 4 + state 12 read, "
+                     "state 12 + bf16 2 written); d2h copies the fp32 gradient, h2d the bf16 parameters"}
+    if not context:
+        return parts
     # the reduce kernel writing one chunk straight into pinned host memory
     chunk = [r[:C] for r in st["reps"]]
     h_g = b["h_grad"][:C]
@@ -795,15 +803,11 @@ def offload_parts(st):
             times[k].append((time.perf_counter() - t0) * 1e3)
             st["t"] += 1
     del other
-    return {"chunk_elems": C, "host_threads": OFFLOAD_THREADS,
-            "host_update_gbs": 30 * C / host_s / 1e9, "host_update_params_per_s": C / host_s,
-            "d2h_gbs": 4 * C / d2h_ms / 1e6, "h2d_gbs": 2 * C / h2d_ms / 1e6,
-            "d2h_by_kernel_gbs": 4 * C / kd2h_ms / 1e6,
-            "step_ms_by_staging": {k: round(sorted(v)[len(v) // 2], 2) for k, v in times.items()},
-            "note": "host update moves 30 B per element in host memory (grad 4 + state 12 read, "
-                    "state 12 + bf16 2 written); d2h copies the fp32 gradient, h2d the bf16 parameters; "
-                    "d2h_by_kernel: the reduce kernel writes the chunk into pinned host memory itself; "
-                    "step_ms_by_staging: the upper median of 4 whole steps each, interleaved"}
+    parts["d2h_by_kernel_gbs"] = 4 * C / kd2h_ms / 1e6
+    parts["step_ms_by_staging"] = {k: round(sorted(v)[len(v) // 2], 2) for k, v in times.items()}
+    parts["note"] += ("; d2h_by_kernel: the reduce kernel writes the chunk into pinned host memory "
+                      "itself; step_ms_by_staging: the upper median of 4 whole steps each, interleaved")
+    return parts
 
 
 def hparams(st):
@@ -992,7 +996,7 @@ def main(argv=None):
                          "its own allocation")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context legs (copy ceiling, separate-placement step, cold launches, graph "
-                         "replay), "
+                         "replay, the offloaded step's direct-staging legs), "
                          "so that a profiler sees only the timed step's launches")
     ap.add_argument("--offload-staging", default="copy", choices=["copy", "direct"],
                     help="offload7b: gradient chunks reduced into device staging and copied to pinned "
@@ -1087,7 +1091,7 @@ def main(argv=None):
         for _ in range(10):
             spans("k_reduce", lambda: Z.zero_reduce_shard(chunk, OFFLOAD_CHUNK, d_g))
         torch.cuda.synchronize()
-        parts = offload_parts(st)
+        parts = offload_parts(st, context=not args.no_context)
     for k in kernels:
         xs = spans.ms(k)
         if not xs:                         # e.g. the update pass of steps that were all skipped

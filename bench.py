@@ -10,14 +10,18 @@ zero_arena_layout (arrays a kernel walks together start at staggered offsets pas
 
 Prints one JSON line (see the fields below). Flags:
   --gpus N         only 1 is supported: this path runs on one GPU's shard
-  --steps K        timed steps (default 20)
+  --steps K        timed steps (default: per workload, a timed region of a few seconds, e.g.
+                   1000 for llama7b)
   --warmup W       untimed steps first (default 3)
   --config C       the same by config number: 2 gpt2, 3 llama7b, 4 llama13b, 5 gpt3
   --workload NAME  llama7b (default), gpt2, llama13b (two-pass clip path), gpt3 (64 Mi windows),
                    gather7b (ZeRO-3: every Llama-7B layer gathered from its 8 rank shards),
                    offload7b (ZeRO-Offload: the 7B shard's Adam state in host memory)
   --placement P    arena (default) or separate: every array of the step in its own allocation
-  --no-context     skip the context legs (copy ceiling, separate-placement step, cold launches, graph replay)
+  --no-context     skip the context legs (copy ceiling, separate-placement step, cold launches, graph
+                   replay, the offloaded step's direct-staging legs)
+  --offload-staging copy|direct  offload7b: gradient chunks copied from device staging (default) or
+                   written into pinned host memory by the reduce kernel
   --cpu-seconds S  budget of the oracle's CPU baseline (default 12; 0 skips it)
   --copy-calib MB  also run a plain device copy of MB MiB 5 times (for counter calibration)
   --summarize      (no GPU) turn the rocprofv3 CSVs of the profile commands into the summaries

@@ -170,8 +170,9 @@ def launch_elems(workload: str) -> float:
     from workloads import WORKLOADS
     if workload == "gather7b":
         return WORKLOADS["llama7b"].n / GATHER_LAYERS
-    if workload == "offload7b":
-        return OFFLOAD_CHUNK
+    if workload == "offload7b":         # the step's chunks: 25 of 32 Mi and a shorter last one
+        S = shard_elems(WORKLOADS["llama7b"])
+        return S / -(-S // OFFLOAD_CHUNK)
     w = WORKLOADS["llama13b" if workload.startswith("llama13b") else workload]
     S = shard_elems(w)
     return S / -(-S // (w.window or S))
@@ -1084,16 +1085,20 @@ def main(argv=None):
     per_kernel = {}
     parts = None
     if args.workload == "offload7b":
-        # the reduce kernel runs inside the offloaded call; time it alone on one chunk
+        # the reduce kernel runs inside the offloaded call; time it alone over the chunks one step
+        # walks (so the mean launch is launch_elems' and a profiled run sees only whole sequences)
         import zero_partition_plan_amd as Z
         d_g = st["bufs"]["d_grad"]
         if d_g is None:                    # direct staging: time the kernel into device memory here
             d_g = torch.empty(OFFLOAD_CHUNK, dtype=torch.float32, device="cuda")
-        chunk = [r[:OFFLOAD_CHUNK] for r in st["reps"]]      # built outside the timed spans
+        # (marshalled once, so that the host keeps ahead of 0.1 ms launches)
+        calls = [Z.ReduceCall([r[a:min(S, a + OFFLOAD_CHUNK)] for r in st["reps"]],
+                              min(S, a + OFFLOAD_CHUNK) - a, d_g) for a in range(0, S, OFFLOAD_CHUNK)]
+        for call in calls:
+            call()
         for _ in range(2):
-            Z.zero_reduce_shard(chunk, OFFLOAD_CHUNK, d_g)
-        for _ in range(10):
-            spans("k_reduce", lambda: Z.zero_reduce_shard(chunk, OFFLOAD_CHUNK, d_g))
+            for call in calls:
+                spans("k_reduce", call)
         torch.cuda.synchronize()
         parts = offload_parts(st, context=not args.no_context)
     for k in kernels:

@@ -703,6 +703,32 @@ def test_prepared_step_equals_the_plain_call():
         assert_bits_equal(b, a, what)
 
 
+def test_prepared_reduce_equals_the_plain_call():
+    """ReduceCall (arrays marshalled once) writes the gradient, flag and partials zero_reduce_shard
+    writes, call after call, over several tiles and a ragged tail."""
+    n = 6 * TILE + 91
+    rng = np.random.default_rng(45)
+    reps = _reps_np(rng, 5, n, "f16")
+    d_r = [dev_rep(r, "f16") for r in reps]
+    runs = []
+    for prepared in (False, True):
+        g = torch.full((n,), float("nan"), device=DEV)
+        flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+        parts = torch.full((Z.zero_sq_partials_len(n),), -1.0, dtype=torch.float64, device=DEV)
+        call = Z.ReduceCall(d_r, n, g, flag, parts) if prepared else None
+        for scale in (2.0 ** -16, 0.5):
+            if prepared:
+                call(scale)
+            else:
+                Z.zero_reduce_shard(d_r, n, g, flag, parts, scale)
+        torch.cuda.synchronize()
+        runs.append((bits32(g), int(flag.item()), parts.cpu().numpy().view(np.uint64).copy()))
+    assert_bits_equal(runs[1][0], runs[0][0], "gradient")
+    assert runs[1][1] == runs[0][1] == 0
+    assert np.array_equal(runs[1][2], runs[0][2])
+    assert_bits_equal(runs[1][0], f32_bits(O.replica_sum(list(reps), "f16")), "gradient vs oracle")
+
+
 def test_concurrent_steps_from_host_threads():
     """Six host threads, each with its own stream and arrays, step at the same time: every result
     equals the oracle's bit for bit (launch setup, the CU-count cache and error state are safe to use

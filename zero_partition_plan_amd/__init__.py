@@ -28,7 +28,7 @@ __all__ = [
     "ZERO_STATIC_SQ_PARTIALS", "ZERO_STATIC_MAX_ELEMS", "zero_adam_shard_step",
     "zero_adam_shard_step_dev_scale", "zero_clip_scale", "zero_adam_derive_table", "adam_table",
     "zero_adam_shard_step_dev_t",
-    "AdamStep",
+    "AdamStep", "ReduceCall",
     "zero_gather_params", "zero_host_adam_step", "zero_offload_step",
     "zero_status_str", "zero_last_error",
 ]
@@ -452,6 +452,25 @@ class AdamStep:
         n, p, m, v = self._args
         _check(self._fn(self._ref, n, grad_scale, p, m, v, ctypes.byref(hp), *self._tail),
                "zero_adam_shard_step")
+
+
+class ReduceCall:
+    """zero_reduce_shard with its arrays and stream marshalled once; a call passes only sq_scale.
+    For loops of launches short enough that per-call marshalling shows. The tensors must stay alive
+    and in place while it is used."""
+
+    def __init__(self, reps, n: int, out_grad=None, nonfinite=None, sq_partials=None, stream=None):
+        self._src, self._keep = _src(reps, n)
+        self._tensors = (reps, out_grad, nonfinite, sq_partials)
+        self._fn = lib().zero_reduce_shard
+        self._args = (ctypes.byref(self._src), n,
+                      _ptr(out_grad, n, "out_grad", (torch.float32,), pinned_ok=True),
+                      _ptr(nonfinite, 1, "nonfinite", (torch.int32,)),
+                      _ptr(sq_partials, zero_sq_partials_len(n), "sq_partials", (torch.float64,)))
+        self._stream = _stream(stream)
+
+    def __call__(self, sq_scale: float = 1.0):
+        _check(self._fn(*self._args, float(sq_scale), self._stream), "zero_reduce_shard")
 
 
 def zero_gather_params(shards, begin: int, count: int, out, stream=None):

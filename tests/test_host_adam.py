@@ -189,3 +189,37 @@ def test_host_step_array_phases(odt, mode):
             if odt:
                 keep[oo:oo + n] = False
             assert (out[keep] == 0x5A5A).all(), what
+
+
+@pytest.mark.parametrize("odt", ["bf16", "f16"])
+def test_host_step_ignores_callers_flush_to_zero(odt):
+    """A caller running with flush-to-zero and denormals-are-zero (torch.set_flush_denormal) gets
+    the IEEE results all the same: the host update sets IEEE mode in every thread it runs on, and
+    the caller's mode is back afterwards. The state is put where the update and the casts meet
+    subnormals: fp32 subnormal parameters and moments, and parameters in binary16's subnormal range."""
+    import torch
+    rng = np.random.default_rng(23)
+    n = 70_001
+    sub32 = (rng.integers(1, 1 << 23, n, dtype=np.uint64).astype(np.uint32)
+             | (rng.integers(0, 2, n, dtype=np.uint64).astype(np.uint32) << 31)).view(np.float32)
+    sub16 = (rng.standard_normal(n) * 3e-6).astype(np.float32)        # binary16 subnormals
+    master = np.where(rng.random(n) < 0.5, sub32, sub16).astype(np.float32)
+    g = (rng.standard_normal(n) * 1e-30).astype(np.float32)
+    m = sub32[::-1].copy()
+    v = np.abs(sub32)
+    hp = {**HP, "step": 2}
+    wp, wm, wv, wo = O.sharded_step([g], "f32", 1.0, master, m, v, O.AdamHParams(**hp), odt)
+    if not torch.set_flush_denormal(True):
+        pytest.skip("this CPU has no flush-to-zero control")
+    try:
+        p2, m2, v2, out = master.copy(), m.copy(), v.copy(), np.zeros(n, np.uint16)
+        Z.zero_host_adam_step(g, n, 1.0, p2, m2, v2, Z.adam_hparams(**hp), out=out,
+                              out_dtype=Z.ZERO_BF16 if odt == "bf16" else Z.ZERO_F16, threads=4)
+        flushed = float(np.float32(1e-40) * np.float32(1.0)) == 0.0       # the caller's mode is back
+    finally:
+        torch.set_flush_denormal(False)
+    assert flushed
+    assert np.array_equal(p2.view(np.uint32), wp.view(np.uint32))
+    assert np.array_equal(m2.view(np.uint32), wm.view(np.uint32))
+    assert np.array_equal(v2.view(np.uint32), wv.view(np.uint32))
+    assert np.array_equal(out, wo)

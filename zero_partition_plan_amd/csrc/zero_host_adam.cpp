@@ -1,8 +1,8 @@
 // Host half of ZeRO-Offload: the Adam/AdamW update on host-resident state ("ZeRO 优化器：把显存
 // “分”着用", ZeRO-Offload: the CPU updates the optimizer state kept in host memory). The same fp32
 // operation order as the GPU kernel, each operation rounded on its own (built with
-// -ffp-contract=off; x86 division and square root are correctly rounded), so the two agree bit for
-// bit. The range is split over host threads. On CPUs with AVX2 and F16C the loop is written with
+// -ffp-contract=off; x86 division and square root are correctly rounded; each thread's range runs
+// in IEEE mode whatever the caller's), so the two agree bit for bit. The range is split over host threads. On CPUs with AVX2 and F16C the loop is written with
 // vector intrinsics and streaming (non-temporal) stores: the state and the 16-bit parameters go
 // straight to memory instead of being read for ownership into the caches, which the update, bound
 // by host memory, turns into time. No HIP calls: this file also builds with a plain host compiler
@@ -84,13 +84,31 @@ inline __attribute__((always_inline)) void adam_range(const HostStep& s, uint64_
   }
 }
 
+// The SSE control register of the running thread set to IEEE behaviour (round to nearest, no
+// flush-to-zero, no denormals-are-zero) for the scope, and restored after it, so the update gives
+// the kernel's bits whatever floating-point mode the caller's threads (and so the worker threads,
+// which start with a copy of it) run in.
+class IeeeScope {
+ public:
+  IeeeScope() : saved_(_mm_getcsr()) { _mm_setcsr(saved_ & ~kNonIeee); }
+  ~IeeeScope() { _mm_setcsr(saved_); }
+  IeeeScope(const IeeeScope&) = delete;
+  IeeeScope& operator=(const IeeeScope&) = delete;
+
+ private:
+  static constexpr unsigned kNonIeee = 0x8000u | 0x6000u | 0x0040u;  // FTZ, rounding control, DAZ
+  unsigned saved_;
+};
+
 template <bool L2, int ODT>
 void range_base(const HostStep& s, uint64_t lo, uint64_t hi) {
+  IeeeScope ieee;
   adam_range<L2, ODT>(s, lo, hi);
 }
 
 template <bool L2, int ODT>
 __attribute__((target("avx2"))) void range_avx2(const HostStep& s, uint64_t lo, uint64_t hi) {
+  IeeeScope ieee;
   adam_range<L2, ODT>(s, lo, hi);
 }
 
@@ -149,6 +167,7 @@ __attribute__((target("avx2,f16c"))) void stream_body(const HostStep& s, uint64_
 // the caller hands the results on (to another thread, or to a DMA copy) after this returns.
 template <bool L2, int ODT>
 __attribute__((target("avx2,f16c"))) void range_stream(const HostStep& s, uint64_t lo, uint64_t hi) {
+  IeeeScope ieee;
   const auto phase = [](const void* p) { return reinterpret_cast<uintptr_t>(p) & 31u; };
   if (phase(s.M + lo) != phase(s.P + lo) || phase(s.V + lo) != phase(s.P + lo)) {
     adam_range<L2, ODT>(s, lo, hi);

@@ -223,3 +223,32 @@ def test_host_step_ignores_callers_flush_to_zero(odt):
     assert np.array_equal(m2.view(np.uint32), wm.view(np.uint32))
     assert np.array_equal(v2.view(np.uint32), wv.view(np.uint32))
     assert np.array_equal(out, wo)
+
+
+def test_host_arithmetic_ignores_callers_rounding_mode():
+    """Under each directed rounding mode set by the caller (C fesetround), the derived step
+    constants and the host update equal their round-to-nearest results bit for bit, and the caller's
+    mode is back afterwards."""
+    import ctypes
+    libc = ctypes.CDLL(None)
+    modes = {"downward": 0x400, "upward": 0x800, "toward zero": 0xC00}       # x86 <fenv.h> values
+    rng = np.random.default_rng(29)
+    n = 20_003
+    master, g, m, v = _case(rng, n)
+    hp = Z.adam_hparams(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=777)
+    want_k = Z.zero_adam_derive(hp)
+    want = [a.copy() for a in (master, m, v)] + [np.zeros(n, np.uint16)]
+    Z.zero_host_adam_step(g, n, 0.25, *want[:3], hp, out=want[3], threads=3)
+    for name, mode in modes.items():
+        got = [a.copy() for a in (master, m, v)] + [np.zeros(n, np.uint16)]
+        assert libc.fesetround(mode) == 0
+        try:
+            k = Z.zero_adam_derive(hp)
+            Z.zero_host_adam_step(g, n, 0.25, *got[:3], hp, out=got[3], threads=3)
+            back = libc.fegetround()
+        finally:
+            libc.fesetround(0)
+        assert back == mode, name
+        assert bytes(k) == bytes(want_k), name
+        for a, b in zip(got, want):
+            assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), name

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "zero_fpenv.h"
 #include "zero_internal.h"
 
 namespace zero {
@@ -202,6 +203,7 @@ zero_status zero_adam_derive(const zero_adam_hparams* hp, zero_adam_scalars* out
     return fail(ZERO_E_INVAL, "zero_adam_derive: lr, eps and weight_decay must be finite and >= 0");
   if (hp->wd_mode != ZERO_ADAMW && hp->wd_mode != ZERO_ADAM_L2)
     return fail(ZERO_E_INVAL, "zero_adam_derive: unknown wd_mode %d", hp->wd_mode);
+  const zero::IeeeScope ieee;   // round to nearest, subnormals kept, whatever the caller's mode
   const double t = (double)hp->step;
   out->b1 = (float)hp->beta1;
   out->b2 = (float)hp->beta2;

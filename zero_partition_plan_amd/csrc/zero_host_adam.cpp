@@ -14,6 +14,7 @@
 #include <thread>
 #include <vector>
 
+#include "zero_fpenv.h"
 #include "zero_host_adam.h"
 
 namespace {
@@ -84,21 +85,7 @@ inline __attribute__((always_inline)) void adam_range(const HostStep& s, uint64_
   }
 }
 
-// The SSE control register of the running thread set to IEEE behaviour (round to nearest, no
-// flush-to-zero, no denormals-are-zero) for the scope, and restored after it, so the update gives
-// the kernel's bits whatever floating-point mode the caller's threads (and so the worker threads,
-// which start with a copy of it) run in.
-class IeeeScope {
- public:
-  IeeeScope() : saved_(_mm_getcsr()) { _mm_setcsr(saved_ & ~kNonIeee); }
-  ~IeeeScope() { _mm_setcsr(saved_); }
-  IeeeScope(const IeeeScope&) = delete;
-  IeeeScope& operator=(const IeeeScope&) = delete;
-
- private:
-  static constexpr unsigned kNonIeee = 0x8000u | 0x6000u | 0x0040u;  // FTZ, rounding control, DAZ
-  unsigned saved_;
-};
+using zero::IeeeScope;
 
 template <bool L2, int ODT>
 void range_base(const HostStep& s, uint64_t lo, uint64_t hi) {

@@ -366,7 +366,8 @@ zero_status zero_host_adam_step(const float* grad, uint64_t n, float grad_scale,
 typedef struct {
   float* d_grad;        /* device float[2 * chunk_elems]: reduced-gradient chunks, or NULL: the
                            reduce kernel then writes each chunk straight into h_grad over the host
-                           link, with no device staging and no copy */
+                           link, with no device staging and no copy (h_grad must then be pinned
+                           and mapped for the device: checked, ZERO_E_INVAL otherwise) */
   float* h_grad;        /* pinned host float[2 * chunk_elems] (hipHostMalloc, so that the device can
                            write it): the chunks the host updates from */
   void* h_param;        /* pinned host 16-bit [2 * chunk_elems]: updated parameters */

@@ -155,3 +155,29 @@ def test_reduce_into_pinned_host_memory():
     assert_bits_equal(h.numpy().view(np.uint32), f32_bits(O.replica_sum(list(reps), "bf16")), "pinned vs oracle")
     with pytest.raises(TypeError):
         Z.zero_reduce_shard(d_reps, n, torch.empty(n, dtype=torch.float32))
+
+
+def test_offload_direct_staging_refuses_pageable_host_memory():
+    """With no device staging the kernel would write h_grad itself, so pageable host memory there
+    is refused before anything is enqueued (the state and the slot are left as they were); pinned
+    memory of the same size is taken."""
+    n = 1000
+    rng = np.random.default_rng(8)
+    reps, master, m, v = _inputs(rng, n, 2)
+    d_reps = [dev_rep(r, "bf16") for r in reps]
+    hm, hmm, hv = master.copy(), m.copy(), v.copy()
+    slot = torch.full((n,), 7.0, dtype=torch.bfloat16, device=DEV)
+    bufs = Z.offload_buffers(256, threads=2, direct=True)
+    bufs["h_grad"] = torch.empty(2 * 256, dtype=torch.float32)           # pageable
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_offload_step(d_reps, n, 1.0, hm, hmm, hv, Z.adam_hparams(**HP), slot, bufs)
+    assert e.value.status == Z.ZERO_E_INVAL and "pinned host memory" in str(e.value)
+    torch.cuda.synchronize()
+    assert np.array_equal(hm, master) and np.array_equal(hmm, m) and np.array_equal(hv, v)
+    assert (slot == 7.0).all()
+    bufs["h_grad"] = torch.empty(2 * 256, dtype=torch.float32, pin_memory=True)
+    Z.zero_offload_step(d_reps, n, 1.0, hm, hmm, hv, Z.adam_hparams(**HP), slot, bufs)
+    torch.cuda.synchronize()
+    p2, _, _, o2 = O.sharded_step(list(reps), "bf16", 1.0, master, m, v, O.AdamHParams(**HP), "bf16")
+    assert_bits_equal(hm.view(np.uint32), f32_bits(p2), "host master")
+    assert_bits_equal(bits16(slot), o2, "slot")

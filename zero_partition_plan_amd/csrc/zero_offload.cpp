@@ -53,6 +53,20 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
     if (zero::overlaps(red, 2 * C * 4, src->ptrs[r], n * rb))
       return zero::fail(ZERO_E_INVAL, "%s: the gradient staging overlaps replica %u", fn, r);
   }
+  if (direct) {
+    // The reduce kernel writes h_grad itself: it must be pinned host memory that the device sees at
+    // the same address (pageable memory would fault the kernel). Both ends of the range are asked.
+    const char* ends[2] = {reinterpret_cast<const char*>(buf->h_grad),
+                           reinterpret_cast<const char*>(buf->h_grad + 2 * C) - 1};
+    for (const char* p : ends) {
+      hipPointerAttribute_t a{};
+      const hipError_t pe = hipPointerGetAttributes(&a, p);
+      (void)hipGetLastError();
+      if (pe != hipSuccess || a.type != hipMemoryTypeHost || a.devicePointer != p)
+        return zero::fail(ZERO_E_INVAL, "%s: with no device staging, h_grad[0, 2 * chunk_elems) must "
+                          "be pinned host memory mapped for the device (hipHostMalloc)", fn);
+    }
+  }
 
   hipStream_t main = static_cast<hipStream_t>(stream);
   hipStream_t back = buf->h2d_stream ? static_cast<hipStream_t>(buf->h2d_stream) : main;

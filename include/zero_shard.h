@@ -209,7 +209,8 @@ uint64_t zero_sq_partials_len(uint64_t n);
  * Stage 2): acc[i] = rep_0[i] + rep_1[i] + ... in ascending order, fp32 accumulator, each 16-bit
  * replica widened exactly. Optional outputs, any subset but at least one:
  *   out_grad      float[n]: acc. Device memory, or pinned host memory (hipHostMalloc), which the
- *                 kernel then writes over the host link (the offloaded step's direct staging).
+ *                 kernel then writes over the host link (the offloaded step's direct staging);
+ *                 never pageable host memory, which the kernel cannot write (not checked here).
  *   d_nonfinite   device int32: set to 1 if any acc[i] is +-inf or NaN, otherwise left as is
  *                 (so several calls OR into it; the caller zeroes it first).
  *   d_sq_partials device double[zero_sq_partials_len(n)]: entry t (t < ceil(n/256)) receives

@@ -140,6 +140,52 @@ def test_llama7b_shard_full_size(slot_off):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("direct", [False, True])
+def test_llama7b_offloaded_step_full_size(direct):
+    """The 7B shard's step offloaded as the benchmark runs it (ZeRO-Offload): master, m and v in
+    host memory, 32 Mi-element chunks, 16 host threads, the gradient chunks copied from device
+    staging or (direct) written into pinned host memory by the reduce kernel. Every element of the
+    host state and of the device slot checked bit for bit against the oracle; the elements just
+    outside the slot keep their canary."""
+    w = WORKLOADS["llama7b"]
+    plan = Z.zero_partition_plan(w.n, w.nd)
+    r = w.ranks[0]
+    begin, valid = Z.zero_shard_range(plan, r)
+    S = plan.shard_elems
+    banner(f"llama7b offloaded rank {r}: S={S} direct={direct}")
+    inp = D.rank_inputs(w, begin, S, valid, device=DEV)
+    host = {k: inp[k].cpu().numpy() for k in ("master", "m", "v")}
+    pre = {k: a.copy() for k, a in host.items()}
+    del inp["master"], inp["m"], inp["v"]
+    _free()
+    d_out = torch.full((S + 2,), -3.0, dtype=torch.bfloat16, device=DEV)
+    slot = d_out[1:1 + S]
+    hp = _hp(w, w.warm_steps + 1)
+    Z.zero_offload_step(inp["reps"], S, 1.0, host["master"], host["m"], host["v"], Z.adam_hparams(**hp),
+                        slot, Z.offload_buffers(32 << 20, threads=16, direct=direct))
+    torch.cuda.synchronize()
+    ohp = O.AdamHParams(**hp)
+
+    def work(a, b):
+        reps = _bits_to_np(_rows(inp["reps"], a, b), w.rep_dtype)
+        p2, m2, v2, o2 = O.sharded_step(list(reps), w.rep_dtype, 1.0, pre["master"][a:b], pre["m"][a:b],
+                                        pre["v"][a:b], ohp, w.out_dtypes[0])
+        assert_bits_equal(host["master"][a:b].view(np.uint32), f32_bits(p2), f"master [{a},{b})")
+        assert_bits_equal(host["m"][a:b].view(np.uint32), f32_bits(m2), f"m [{a},{b})")
+        assert_bits_equal(host["v"][a:b].view(np.uint32), f32_bits(v2), f"v [{a},{b})")
+        assert_bits_equal(bits16(slot[a:b]), o2, f"params [{a},{b})")
+
+    covered, secs = FS.run_chunks(S, work)
+    banner(f"llama7b offloaded (direct={direct}): {covered} of {S} elements "
+           f"({100.0 * covered / S:.1f}%) bit-exact in {secs:.1f} s")
+    assert covered == S
+    ends = bits16(d_out[0:1]).tolist() + bits16(d_out[S + 1:S + 2]).tolist()
+    assert ends == [int(O.cast_bf16_rne(np.float32([-3.0]))[0])] * 2
+    del inp, host, pre, d_out, slot
+    _free()
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("inject", [False, True])
 def test_llama13b_two_pass_full_size(inject):
     """Llama-13B over 16 ranks: 16 fp16 replicas holding grad * 2^16 (with 0.01% +inf injected in

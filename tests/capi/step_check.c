@@ -6,7 +6,10 @@
  * norm, and the update must equal the host update with that scale; so must the same update with
  * t on the device (zero_adam_shard_step_dev_t), which also advances the counter. Last, the reduce
  * pass with no workspace (zero_reduce_shard_static) against the one with a caller's partials.
- * Exits 0 when all match. */
+ * The offloaded step (zero_offload_step: host state, pinned staging, the caller's four events) must
+ * equal the fused device step too, with the gradient chunks copied from device staging and with
+ * the reduce kernel writing them into pinned host memory; pageable memory for the latter must be
+ * refused before anything is enqueued. Exits 0 when all match. */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -113,6 +116,62 @@ int main(void) {
       if (bad < 5) fprintf(stderr, "element %u differs\n", i);
       ++bad;
     }
+  }
+
+  /* the offloaded step against the fused device step, both stagings */
+  {
+    enum { CH = 4096 }; /* 25 chunks, the last one short */
+    static float p_off[N], m_off[N], v_off[N];
+    static uint16_t out_off[N];
+    float *d_stage, *h_grad, *pageable;
+    uint16_t *h_param, *d_out2;
+    hipEvent_t ev[4];
+    zero_offload_buffers ob;
+    zero_status st;
+    int pass;
+    HIP(hipMalloc((void**)&d_stage, 2 * CH * 4));
+    HIP(hipMalloc((void**)&d_out2, N * 2));
+    HIP(hipHostMalloc((void**)&h_grad, 2 * CH * 4, hipHostMallocDefault));
+    HIP(hipHostMalloc((void**)&h_param, 2 * CH * 2, hipHostMallocDefault));
+    for (k = 0; k < 4; ++k) HIP(hipEventCreateWithFlags(&ev[k], hipEventDisableTiming));
+    memset(&ob, 0, sizeof ob);
+    ob.h_grad = h_grad;
+    ob.h_param = h_param;
+    ob.chunk_elems = CH;
+    ob.threads = 3;
+    for (k = 0; k < 4; ++k) ob.events[k] = ev[k];
+    for (pass = 0; pass < 2; ++pass) {
+      ob.d_grad = pass == 0 ? d_stage : NULL; /* NULL: the reduce kernel writes h_grad itself */
+      memcpy(p_off, p0, sizeof p0);
+      memcpy(m_off, m0, sizeof m0);
+      memcpy(v_off, v0, sizeof v0);
+      HIP(hipMemset(d_out2, 0, N * 2));
+      ZS(zero_offload_step(&src, N, gs, p_off, m_off, v_off, &hp, d_out2, ZERO_BF16, &ob, NULL));
+      HIP(hipMemcpy(out_off, d_out2, N * 2, hipMemcpyDeviceToHost));
+      for (i = 0; i < N; ++i) {
+        if (memcmp(&p_off[i], &p_dev[i], 4) || memcmp(&m_off[i], &m_dev[i], 4) ||
+            memcmp(&v_off[i], &v_dev[i], 4) || out_off[i] != out_dev[i]) {
+          if (bad < 5) fprintf(stderr, "offload (%s) element %u differs\n", pass ? "direct" : "copy", i);
+          ++bad;
+        }
+      }
+    }
+    pageable = malloc(2 * CH * 4);
+    if (!pageable) return 2;
+    ob.d_grad = NULL;
+    ob.h_grad = pageable;
+    memcpy(p_off, p0, sizeof p0);
+    st = zero_offload_step(&src, N, gs, p_off, m_off, v_off, &hp, d_out2, ZERO_BF16, &ob, NULL);
+    if (st != ZERO_E_INVAL || memcmp(p_off, p0, sizeof p0)) {
+      fprintf(stderr, "direct staging into pageable memory: status %d (%s)\n", (int)st, zero_last_error());
+      ++bad;
+    }
+    free(pageable);
+    for (k = 0; k < 4; ++k) HIP(hipEventDestroy(ev[k]));
+    HIP(hipHostFree(h_grad));
+    HIP(hipHostFree(h_param));
+    HIP(hipFree(d_stage));
+    HIP(hipFree(d_out2));
   }
 
   /* the clipped path: squared norm of the reduced gradient, clip scale and update on the device */

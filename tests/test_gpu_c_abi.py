@@ -4,8 +4,10 @@ the clipped path enqueued with nothing read back (squared norm, zero_clip_scale,
 zero_adam_shard_step_dev_scale) gives C's own double evaluation of the clip rule and the host
 update's bits, and so does the same update with t on the device (zero_adam_shard_step_dev_t),
 which advances the counter, and the reduce pass with no workspace (zero_reduce_shard_static) equals
-the one with a caller's partials (tests/capi/step_check.c). The reduce pass and the host update are each
-pinned to the oracle by the other tests."""
+the one with a caller's partials; the offloaded step (zero_offload_step with the caller's pinned
+staging and events) equals the fused step with either staging, and refuses pageable memory for
+direct staging (tests/capi/step_check.c). The reduce pass and the host update are each pinned to
+the oracle by the other tests."""
 
 import os
 import shutil

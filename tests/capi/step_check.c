@@ -9,7 +9,9 @@
  * The offloaded step (zero_offload_step: host state, pinned staging, the caller's four events) must
  * equal the fused device step too, with the gradient chunks copied from device staging and with
  * the reduce kernel writing them into pinned host memory; pageable memory for the latter must be
- * refused before anything is enqueued. Exits 0 when all match. */
+ * refused before anything is enqueued. And the ZeRO-3 gather (zero_gather_params) of a range across
+ * the replica buffers taken as rank shards must equal the host's concatenation of them. Exits 0
+ * when all match. */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -116,6 +118,24 @@ int main(void) {
       if (bad < 5) fprintf(stderr, "element %u differs\n", i);
       ++bad;
     }
+  }
+
+  /* the ZeRO-3 gather: flat [N - 100, 2N + 50) of the replica buffers laid end to end */
+  {
+    enum { GB = N - 100, GC = N + 150 };
+    static uint16_t g_out[GC];
+    uint16_t* d_gout;
+    HIP(hipMalloc((void**)&d_gout, GC * 2));
+    ZS(zero_gather_params(d_rep_ptrs, R, N, 2, GB, GC, d_gout, NULL));
+    HIP(hipMemcpy(g_out, d_gout, GC * 2, hipMemcpyDeviceToHost));
+    for (i = 0; i < GC; ++i) {
+      const uint32_t j = GB + i;
+      if (g_out[i] != reps[j / N][j % N]) {
+        if (bad < 5) fprintf(stderr, "gather element %u differs\n", i);
+        ++bad;
+      }
+    }
+    HIP(hipFree(d_gout));
   }
 
   /* the offloaded step against the fused device step, both stagings */

@@ -10,8 +10,9 @@
  * equal the fused device step too, with the gradient chunks copied from device staging and with
  * the reduce kernel writing them into pinned host memory; pageable memory for the latter must be
  * refused before anything is enqueued. And the ZeRO-3 gather (zero_gather_params) of a range across
- * the replica buffers taken as rank shards must equal the host's concatenation of them. Exits 0
- * when all match. */
+ * the replica buffers taken as rank shards must equal the host's concatenation of them, and the
+ * fused step with all its arrays in one arena (zero_arena_layout, zero_arena_alloc) must equal the
+ * step on separate allocations. Exits 0 when all match. */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -116,6 +117,53 @@ int main(void) {
     if (memcmp(&p_dev[i], &p_host[i], 4) || memcmp(&m_dev[i], &m_host[i], 4) ||
         memcmp(&v_dev[i], &v_host[i], 4) || out_dev[i] != out_host[i]) {
       if (bad < 5) fprintf(stderr, "element %u differs\n", i);
+      ++bad;
+    }
+  }
+
+  /* the fused step with every array in one arena placed by zero_arena_layout */
+  {
+    static float pa[N], ma[N], va[N];
+    static uint16_t oa[N];
+    zero_arena_array arr[R + 4];
+    uint64_t off[R + 4], total = 0;
+    const void* a_reps[R];
+    zero_grad_src src_a;
+    char* base = NULL;
+    int32_t contiguous = -1;
+    for (k = 0; k < R + 4; ++k) {
+      arr[k].bytes = (uint64_t)N * (k <= R ? 2 : 4); /* R replicas and the slot, then master, m, v */
+      arr[k].hot_offset = 0;
+      arr[k].group = k <= R ? 0 : 1;
+      arr[k].elem_bytes = k <= R ? 2 : 4;
+    }
+    ZS(zero_arena_layout(arr, R + 4, off, &total));
+    ZS(zero_arena_alloc(total, (void**)&base, &contiguous));
+    for (k = 0; k < R; ++k) {
+      HIP(hipMemcpy(base + off[k], reps[k], N * 2, hipMemcpyHostToDevice));
+      a_reps[k] = base + off[k];
+    }
+    HIP(hipMemcpy(base + off[R + 1], p0, N * 4, hipMemcpyHostToDevice));
+    HIP(hipMemcpy(base + off[R + 2], m0, N * 4, hipMemcpyHostToDevice));
+    HIP(hipMemcpy(base + off[R + 3], v0, N * 4, hipMemcpyHostToDevice));
+    src_a.ptrs = a_reps;
+    src_a.count = R;
+    src_a.dtype = ZERO_BF16;
+    ZS(zero_adam_shard_step(&src_a, N, gs, (float*)(base + off[R + 1]), (float*)(base + off[R + 2]),
+                            (float*)(base + off[R + 3]), &hp, base + off[R], ZERO_BF16, NULL, NULL));
+    HIP(hipDeviceSynchronize());
+    HIP(hipMemcpy(pa, base + off[R + 1], N * 4, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(ma, base + off[R + 2], N * 4, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(va, base + off[R + 3], N * 4, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(oa, base + off[R], N * 2, hipMemcpyDeviceToHost));
+    ZS(zero_arena_free(base));
+    if (contiguous != 0 && contiguous != 1) {
+      fprintf(stderr, "zero_arena_alloc: contiguous flag %d\n", (int)contiguous);
+      ++bad;
+    }
+    if (memcmp(pa, p_dev, sizeof pa) || memcmp(ma, m_dev, sizeof ma) || memcmp(va, v_dev, sizeof va) ||
+        memcmp(oa, out_dev, sizeof oa)) {
+      fprintf(stderr, "the step in an arena differs from the step on separate allocations\n");
       ++bad;
     }
   }

@@ -6,7 +6,8 @@ update's bits, and so does the same update with t on the device (zero_adam_shard
 which advances the counter, and the reduce pass with no workspace (zero_reduce_shard_static) equals
 the one with a caller's partials; the offloaded step (zero_offload_step with the caller's pinned
 staging and events) equals the fused step with either staging, and refuses pageable memory for
-direct staging; and the ZeRO-3 gather of a range across shards equals their concatenation
+direct staging; the ZeRO-3 gather of a range across shards equals their concatenation; and the
+fused step in an arena (zero_arena_layout, zero_arena_alloc) equals it on separate allocations
 (tests/capi/step_check.c). The reduce pass and the host update are each pinned to
 the oracle by the other tests."""
 

@@ -61,7 +61,7 @@ zero_status zero_offload_step(const zero_grad_src* src, uint64_t n, float grad_s
     for (const char* p : ends) {
       hipPointerAttribute_t a{};
       const hipError_t pe = hipPointerGetAttributes(&a, p);
-      (void)hipGetLastError();
+      if (pe != hipSuccess) (void)hipGetLastError();   // clear only the error this query set
       if (pe != hipSuccess || a.type != hipMemoryTypeHost || a.devicePointer != p)
         return zero::fail(ZERO_E_INVAL, "%s: with no device staging, h_grad[0, 2 * chunk_elems) must "
                           "be pinned host memory mapped for the device (hipHostMalloc)", fn);
